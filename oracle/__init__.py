@@ -1,0 +1,26 @@
+"""CPU oracle for the FMHA forward pass (fp64, plain definition).
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. It shares no
+code with the HIP path and imports nothing from it.
+
+Parity status per function:
+  attention / attention_sampled / attention_bruteforce -- pinned (brute force,
+      torch float64 SDPA, closed forms and invariants in tests/test_oracle.py);
+  e4m3_decode / e4m3_encode -- pinned (format definition values, torch
+      float8_e4m3fn casts);
+  attention_fp8pv -- pinned through its parts (decode + attention);
+  attention_fp8pv_emulated -- a diagnostic only; parity unpinned.
+"""
+
+from .reference import (DEFAULT_ROW_BLOCK, attention, attention_bruteforce, attention_rows,
+                        attention_sampled, scores, softmax_rows, visible)
+from .fp8 import (E4M3_MAX, attention_fp8pv, attention_fp8pv_emulated, attention_fp8pv_sampled,
+                  dequantize_v, e4m3_decode, e4m3_encode)
+
+__all__ = [
+    "DEFAULT_ROW_BLOCK", "attention", "attention_bruteforce", "attention_rows",
+    "attention_sampled", "scores", "softmax_rows", "visible", "E4M3_MAX", "attention_fp8pv",
+    "attention_fp8pv_emulated", "attention_fp8pv_sampled", "dequantize_v", "e4m3_decode",
+    "e4m3_encode",
+]
