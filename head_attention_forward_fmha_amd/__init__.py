@@ -1,0 +1,164 @@
+"""MI355X-native fused multi-head attention forward pass (Python binding).
+
+``fwd`` and ``fwd_fp8pv`` marshal torch tensors into the C ABI of libfmha.so
+(include/fmha.h); torch supplies device memory and the current HIP stream, and
+every step of the forward pass runs in the library's gfx950 kernels.
+
+The operation is the FMHA forward pass of the pages ("[BUG] Unexpected Slower
+Performance in C++ CuTe (77_blackwell_fmha) vs Python CuTe DSL (fmha.py) on
+Jetson Thor", Key Observation 2; "CuTe DSL 4.7/4.8 regression: FlashAttention-4
+SM100 forward kernel spills registers", Steps/Code to reproduce bug): packed
+varlen [total, heads, d] bf16 tensors with int32 cu_seqlens, optional causal
+masking, output O and the natural-log LSE of each query row.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import FMHA_OK, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
+
+__all__ = ["fwd", "fwd_fp8pv", "validate_cu_seqlens", "status_string", "abi_version",
+           "FmhaError", "EXPORTED_SYMBOLS", "load_library"]
+
+
+def load_library():
+    return _lib.load()
+
+
+def status_string(status: int) -> str:
+    return _lib.status_string(status)
+
+
+def abi_version() -> int:
+    return int(_lib.load().fmha_abi_version())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, dtype, ndim, device):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+
+
+def _prepare(q, k, v_like, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
+    """Normalise dense [b,s,h,d] / packed [t,h,d] inputs to the C-ABI sizes."""
+    import torch
+    if q.dim() == 4:
+        b, sq, h, d = q.shape
+        sk = k.shape[1]
+        if cu_seqlens_q is not None or cu_seqlens_k is not None:
+            raise ValueError("dense [b, s, h, d] inputs take no cu_seqlens")
+        return dict(batch=b, total_q=b * sq, total_k=b * sk, max_q=sq, max_k=sk, heads=h, d=d,
+                    cu_q=None, cu_k=None, out_shape=(b, sq, h, d), lse_len=b * sq)
+    if q.dim() != 3:
+        raise ValueError("q must be [total, heads, d] or [b, s, heads, d]")
+    tq, h, d = q.shape
+    tk = k.shape[0]
+    if cu_seqlens_q is None:
+        if cu_seqlens_k is not None:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must be given together")
+        return dict(batch=1, total_q=tq, total_k=tk, max_q=tq, max_k=tk, heads=h, d=d,
+                    cu_q=None, cu_k=None, out_shape=(tq, h, d), lse_len=tq)
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu is None or cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 vector")
+        if cu.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if max_seqlen_q is None or max_seqlen_k is None:
+        raise ValueError("max_seqlen_q and max_seqlen_k are required with cu_seqlens")
+    return dict(batch=cu_seqlens_q.numel() - 1, total_q=tq, total_k=tk, max_q=int(max_seqlen_q),
+                max_k=int(max_seqlen_k), heads=h, d=d, cu_q=cu_seqlens_q, cu_k=cu_seqlens_k,
+                out_shape=(tq, h, d), lse_len=tq)
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[int] = None,
+        max_seqlen_k: Optional[int] = None, causal: bool = False,
+        softmax_scale: Optional[float] = None, out=None, lse=None,
+        return_lse: bool = True) -> Tuple:
+    """bf16 FMHA forward. Returns (out, lse) with lse fp32 [heads, total_q].
+
+    q [total_q, h, d] / k, v [total_k, h, d] with cu_seqlens (int32 [batch+1]),
+    or dense q [b, sq, h, d] / k, v [b, sk, h, d]. d must be 64 or 128.
+    """
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, q.dim(), dev)
+    _check_tensor("k", k, torch.bfloat16, q.dim(), dev)
+    _check_tensor("v", v, torch.bfloat16, q.dim(), dev)
+    s = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if k.shape != v.shape or k.shape[-2:] != q.shape[-2:]:
+        raise ValueError("k and v must match, with q's heads and head_dim")
+    scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    st = lib.fmha_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"],
+                      s["total_q"], s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"],
+                      int(bool(causal)), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                      ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_fwd")
+    return out, lse
+
+
+def fwd_fp8pv(q, k, v_e4m3, v_scale, cu_seqlens_q=None, cu_seqlens_k=None,
+              max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+              causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse=None,
+              return_lse: bool = True) -> Tuple:
+    """FMHA forward with P.V in fp8 e4m3. v_e4m3 is uint8 codes, v_scale fp32 [heads]."""
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, q.dim(), dev)
+    _check_tensor("k", k, torch.bfloat16, q.dim(), dev)
+    _check_tensor("v_e4m3", v_e4m3, torch.uint8, q.dim(), dev)
+    _check_tensor("v_scale", v_scale, torch.float32, 1, dev)
+    s = _prepare(q, k, v_e4m3, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if k.shape != v_e4m3.shape or k.shape[-2:] != q.shape[-2:] or v_scale.numel() != s["heads"]:
+        raise ValueError("k, v_e4m3, v_scale shapes do not match q")
+    scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    st = lib.fmha_fwd_fp8pv(_ptr(q), _ptr(k), _ptr(v_e4m3), _ptr(v_scale), _ptr(s["cu_q"]),
+                            _ptr(s["cu_k"]), s["batch"], s["total_q"], s["total_k"], s["max_q"],
+                            s["max_k"], s["heads"], s["d"], int(bool(causal)),
+                            ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                            ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_fwd_fp8pv")
+    return out, lse
+
+
+def validate_cu_seqlens(cu_host, total: int, max_seqlen: int) -> bool:
+    """Host-side check of a cu_seqlens array (numpy/list/CPU tensor) via the C ABI."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    st = _lib.load().fmha_validate_cu_seqlens(arr.ctypes.data_as(ctypes.c_void_p),
+                                              int(arr.size) - 1, int(total), int(max_seqlen))
+    return st == FMHA_OK

@@ -1,0 +1,83 @@
+"""ctypes loader for libfmha.so and the raw C-ABI prototypes (include/fmha.h).
+
+Only argument marshalling lives here; every step of the forward pass runs in
+the HIP kernels of libfmha.so. Loading fails loudly when the library has not
+been built: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfmha.so")
+
+FMHA_OK = 0
+FMHA_ERR_INVALID_ARG = 1
+FMHA_ERR_UNSUPPORTED = 2
+FMHA_ERR_LAUNCH = 3
+
+EXPORTED_SYMBOLS = (
+    "fmha_fwd",
+    "fmha_fwd_fp8pv",
+    "fmha_validate_cu_seqlens",
+    "fmha_status_string",
+    "fmha_abi_version",
+)
+
+_lib = None
+
+_vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+_FWD_ARGS = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+             _vp, _vp, _vp]
+_FWD_FP8_ARGS = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                 _f32, _vp, _vp, _vp]
+
+
+class FmhaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def _single_hip_runtime_check():
+    """The process must hold one HIP runtime; two would not share streams."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise RuntimeError(f"more than one HIP runtime is loaded: {sorted(real)}")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfmha.so (after torch, so that torch's HIP runtime is reused)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m head_attention_forward_fmha_amd.build` "
+            "(there is no non-HIP fallback)")
+    import torch  # noqa: F401  -- load torch's libamdhip64 first
+    lib = ctypes.CDLL(path)
+    lib.fmha_fwd.argtypes = _FWD_ARGS
+    lib.fmha_fwd.restype = ctypes.c_int
+    lib.fmha_fwd_fp8pv.argtypes = _FWD_FP8_ARGS
+    lib.fmha_fwd_fp8pv.restype = ctypes.c_int
+    lib.fmha_validate_cu_seqlens.argtypes = [_vp, _i32, _i32, _i32]
+    lib.fmha_validate_cu_seqlens.restype = ctypes.c_int
+    lib.fmha_status_string.argtypes = [ctypes.c_int]
+    lib.fmha_status_string.restype = ctypes.c_char_p
+    lib.fmha_abi_version.argtypes = []
+    lib.fmha_abi_version.restype = ctypes.c_int32
+    _single_hip_runtime_check()
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fmha_status_string(int(status)).decode()

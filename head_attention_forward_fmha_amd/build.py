@@ -1,0 +1,121 @@
+"""Builds libfmha.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+Usage: python -m head_attention_forward_fmha_amd.build [--verbose]
+
+The library is linked against the HIP runtime with an rpath that prefers
+torch's bundled libamdhip64.so, so that a process which imports torch first
+and then loads this library uses exactly one HIP runtime (both carry the
+SONAME libamdhip64.so.7). The compiler's kernel resource report
+(-Rpass-analysis=kernel-resource-usage) is saved next to the library and
+checked: every kernel must use no scratch and spill no registers.
+"""
+
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libfmha.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+RESOURCE_REPORT = os.path.join(PKG_DIR, "libfmha.resource-usage.txt")
+SOURCES = ["fmha_fwd_kernel.hip", "fmha_api.hip"]
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU ops stay disabled; hipcc -O3 would otherwise form them
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP toolchain is required to build libfmha.so")
+
+
+def _torch_lib_dir():
+    try:
+        import torch
+        return os.path.join(os.path.dirname(torch.__file__), "lib")
+    except Exception:
+        return None
+
+
+def parse_resource_report(text: str) -> dict:
+    """Map kernel name -> {field: value} from clang's kernel-resource-usage remarks."""
+    kernels = {}
+    cur = None
+    for line in text.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark: .*?:\s+([A-Za-z][A-Za-z /\[\]]*?):\s+(\S+) \[-Rpass", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+    return kernels
+
+
+def check_resources(kernels: dict) -> list:
+    """Return a list of violations (scratch use or spills) in a parsed report."""
+    bad = []
+    for name, f in kernels.items():
+        if f.get("ScratchSize [bytes/lane]", "0") != "0":
+            bad.append(f"{name}: scratch {f.get('ScratchSize [bytes/lane]')} B/lane")
+        for key in ("VGPRs Spill", "SGPRs Spill"):
+            if f.get(key, "0") != "0":
+                bad.append(f"{name}: {key} {f[key]}")
+    return bad
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    build_dir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    objs = []
+    reports = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(build_dir, src + ".o")
+        cmd = [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC,
+               "-Rpass-analysis=kernel-resource-usage", "-c", path, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {src}")
+        reports.append(r.stderr)
+        objs.append(obj)
+    rpaths = [d for d in (_torch_lib_dir(), "/opt/rocm/lib") if d]
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+           *[f"-Wl,-rpath,{d}" for d in rpaths]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of libfmha.so failed")
+    os.replace(tmp, LIB_PATH)
+    text = "\n".join(reports)
+    with open(RESOURCE_REPORT, "w") as f:
+        f.write(text)
+    bad = check_resources(parse_resource_report(text))
+    if bad:
+        raise RuntimeError("kernel resource gate failed (scratch or spills):\n  " + "\n  ".join(bad))
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

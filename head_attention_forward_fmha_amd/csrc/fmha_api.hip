@@ -1,0 +1,144 @@
+// C ABI of the FMHA forward library (declared in include/fmha.h).
+//
+// Host-side argument validation happens before any HIP call, so the checks
+// run (and are tested) on machines without a GPU. The library allocates
+// nothing and keeps no state; launches go to the caller's stream.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fmha.h"
+#include "fmha_kernel_params.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by the bf16 and fp8 P.V entry points. Returns FMHA_OK when the
+// arguments describe a launchable problem.
+fmha_status_t check_common(const void* q, const void* k, const void* v,
+                           const int32_t* cu_q, const int32_t* cu_k, int32_t batch,
+                           int32_t total_q, int32_t total_k, int32_t max_q, int32_t max_k,
+                           int32_t heads, int32_t head_dim, int32_t causal, float scale,
+                           const void* out, const float* lse) {
+  if (batch < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return FMHA_ERR_INVALID_ARG;
+  if (heads <= 0) return FMHA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FMHA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FMHA_ERR_INVALID_ARG;
+  if ((cu_q == nullptr) != (cu_k == nullptr)) return FMHA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return FMHA_ERR_UNSUPPORTED;
+  if (cu_q == nullptr) {
+    // dense [batch, seqlen, heads, d]
+    if ((int64_t)batch * max_q != total_q || (int64_t)batch * max_k != total_k) return FMHA_ERR_INVALID_ARG;
+  }
+  // element offsets are computed in 32-bit inside the kernels' inner loops
+  const int64_t row = (int64_t)heads * head_dim;
+  if (row * (int64_t)total_q > INT32_MAX || row * (int64_t)total_k > INT32_MAX ||
+      (int64_t)heads * total_q > INT32_MAX || batch > 65535 || heads > 65535 ||
+      ((int64_t)max_q + 127) / 128 > 65535)
+    return FMHA_ERR_UNSUPPORTED;
+  if (total_q > 0 && (q == nullptr || out == nullptr)) return FMHA_ERR_INVALID_ARG;
+  if (total_k > 0 && (k == nullptr || v == nullptr)) return FMHA_ERR_INVALID_ARG;
+  if ((q && !aligned16(q)) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
+      (out && !aligned16(out)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return FMHA_ERR_INVALID_ARG;
+  return FMHA_OK;
+}
+
+fmha::FwdParams make_params(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                            const int32_t* cu_k, int32_t batch, int32_t total_q,
+                            int32_t total_k, int32_t max_q, int32_t max_k, int32_t heads,
+                            float scale, void* out, float* lse) {
+  fmha::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.cu_q = cu_q;
+  p.cu_k = cu_k;
+  p.v_scale = nullptr;
+  p.out = out;
+  p.lse = lse;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.max_seqlen_q = max_q;
+  p.max_seqlen_k = max_k;
+  p.heads = heads;
+  p.scale_log2 = scale * kLog2e;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+fmha_status_t fmha_fwd(const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int32_t batch, int32_t total_q, int32_t total_k,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t num_heads, int32_t head_dim,
+                       int32_t causal, float softmax_scale,
+                       void* out, float* lse, void* stream) {
+  fmha_status_t st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
+                                  softmax_scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
+  fmha::FwdParams p = make_params(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, softmax_scale, out, lse);
+  hipError_t e = fmha::launch_fwd_bf16(p, head_dim, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3,
+                             const float* v_scale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t total_q, int32_t total_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t num_heads, int32_t head_dim,
+                             int32_t causal, float softmax_scale,
+                             void* out, float* lse, void* stream) {
+  fmha_status_t st = check_common(q, k, v_e4m3, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim,
+                                  causal, softmax_scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (head_dim != 128) return FMHA_ERR_UNSUPPORTED;
+  if (total_k > 0 && v_scale == nullptr) return FMHA_ERR_INVALID_ARG;
+  if (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u)) return FMHA_ERR_INVALID_ARG;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
+  fmha::FwdParams p = make_params(q, k, v_e4m3, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, softmax_scale,
+                                  out, lse);
+  p.v_scale = v_scale;
+  hipError_t e = fmha::launch_fwd_fp8pv(p, head_dim, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+fmha_status_t fmha_validate_cu_seqlens(const int32_t* host_cu, int32_t batch, int32_t total,
+                                       int32_t max_seqlen) {
+  if (batch < 0 || total < 0 || max_seqlen < 0) return FMHA_ERR_INVALID_ARG;
+  if (host_cu == nullptr) return FMHA_ERR_INVALID_ARG;
+  if (host_cu[0] != 0) return FMHA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = (int64_t)host_cu[b + 1] - host_cu[b];
+    if (len < 0 || len > max_seqlen) return FMHA_ERR_INVALID_ARG;
+  }
+  return host_cu[batch] == total ? FMHA_OK : FMHA_ERR_INVALID_ARG;
+}
+
+const char* fmha_status_string(fmha_status_t status) {
+  switch (status) {
+    case FMHA_OK: return "ok";
+    case FMHA_ERR_INVALID_ARG: return "invalid argument";
+    case FMHA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FMHA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t fmha_abi_version(void) { return FMHA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Kernel parameter block shared by the host launcher and the gfx950 kernels.
+#ifndef FMHA_KERNEL_PARAMS_H_
+#define FMHA_KERNEL_PARAMS_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+struct FwdParams {
+  const void* q;          // bf16 [total_q, heads, d]
+  const void* k;          // bf16 [total_k, heads, d]
+  const void* v;          // bf16 or e4m3 [total_k, heads, d]
+  const int32_t* cu_q;    // [batch + 1] or nullptr (dense)
+  const int32_t* cu_k;    // [batch + 1] or nullptr (dense)
+  const float* v_scale;   // [heads] (fp8 P.V only)
+  void* out;              // bf16 [total_q, heads, d]
+  float* lse;             // fp32 [heads, total_q] or nullptr
+  int32_t batch;
+  int32_t total_q;
+  int32_t total_k;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  int32_t heads;
+  float scale_log2;       // softmax_scale * log2(e)
+};
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8pv(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
+
+}  // namespace fmha
+
+#endif  // FMHA_KERNEL_PARAMS_H_

@@ -1,0 +1,130 @@
+/*
+ * fmha.h -- C ABI of the MI355X (gfx950) fused multi-head attention forward pass.
+ *
+ * The operation (sources: "[BUG] Unexpected Slower Performance in C++ CuTe
+ * (77_blackwell_fmha) vs Python CuTe DSL (fmha.py) on Jetson Thor", Key
+ * Observation 2, the softmax_step listings; "CuTe DSL 4.7/4.8 regression:
+ * FlashAttention-4 SM100 forward kernel spills registers", Describe the bug and
+ * the benchmark script under Steps/Code to reproduce bug): for every document b
+ * and head h,
+ *
+ *     S   = softmax_scale * Q_b,h K_b,h^T                 (sq x sk)
+ *     S_ij = -inf where causal and j > i + (sk - sq)       (bottom-right aligned)
+ *     P   = softmax(S) row by row,  O_b,h = P V_b,h,
+ *     LSE_i = ln sum_j exp(S_ij)                            (natural log)
+ *
+ * computed as tiled Q.K^T, an online softmax in the exp2 domain (scale and
+ * running row maximum folded into one multiply-add), and P.V with fp32
+ * accumulation. A query row that sees no key gets O = 0 and LSE = -inf.
+ *
+ * Layout. Tokens of all documents are packed: q, k, v, out are contiguous
+ * row-major [total_tokens, num_heads, head_dim]. Documents are given by int32
+ * prefix arrays cu_seqlens_q / cu_seqlens_k of length batch + 1 (document b
+ * owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1])), as the benchmark script of the
+ * FlashAttention-4 spill issue passes them. When both cu_seqlens pointers are
+ * NULL the input is dense [batch, seqlen, num_heads, head_dim] with
+ * seqlen_q = max_seqlen_q and seqlen_k = max_seqlen_k, which is byte-identical
+ * to the packed layout with uniform documents. lse is fp32 [num_heads, total_q].
+ *
+ * Ownership. The caller allocates and owns every buffer; all pointers except
+ * those documented as host pointers are device pointers on the current HIP
+ * device. The library allocates nothing, keeps no mutable state, is reentrant,
+ * and enqueues its work on `stream` (a hipStream_t; NULL is the legacy default
+ * stream) without synchronising. Outputs are complete once the stream reaches
+ * the enqueued kernel.
+ *
+ * Errors. Argument checks run on the host before any HIP call and return
+ * FMHA_ERR_INVALID_ARG (null or misaligned pointers, negative sizes,
+ * inconsistent dense sizes, non-finite scale) or FMHA_ERR_UNSUPPORTED (a
+ * head_dim other than 64 or 128). A failed launch returns FMHA_ERR_LAUNCH. The
+ * contents of cu_seqlens are a precondition (non-decreasing, starting at 0,
+ * ending at total, every length <= max_seqlen); they are not read on the host,
+ * and fmha_validate_cu_seqlens checks a host copy. Behaviour on violated
+ * preconditions is undefined.
+ */
+#ifndef FMHA_H_
+#define FMHA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FMHA_OK = 0,
+  FMHA_ERR_INVALID_ARG = 1,
+  FMHA_ERR_UNSUPPORTED = 2,
+  FMHA_ERR_LAUNCH = 3
+} fmha_status_t;
+
+/*
+ * bf16 forward pass.
+ *   q            bf16 [total_q, num_heads, head_dim], 16-byte aligned
+ *   k, v         bf16 [total_k, num_heads, head_dim], 16-byte aligned
+ *   cu_seqlens_q int32 [batch + 1] device array, or NULL (dense)
+ *   cu_seqlens_k int32 [batch + 1] device array, or NULL (dense); both NULL or both set
+ *   batch        number of documents (>= 0)
+ *   total_q/k    rows of q and of k/v (dense: batch * max_seqlen_q / _k)
+ *   max_seqlen_q longest query document (sizes the launch grid)
+ *   max_seqlen_k longest key document
+ *   num_heads    > 0
+ *   head_dim     64 or 128
+ *   causal       0 or 1
+ *   softmax_scale fp32 multiplier of Q.K^T (typically 1/sqrt(head_dim))
+ *   out          bf16 [total_q, num_heads, head_dim], 16-byte aligned
+ *   lse          fp32 [num_heads, total_q], or NULL to skip it
+ *   stream       hipStream_t
+ */
+fmha_status_t fmha_fwd(const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int32_t batch, int32_t total_q, int32_t total_k,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t num_heads, int32_t head_dim,
+                       int32_t causal, float softmax_scale,
+                       void* out, float* lse, void* stream);
+
+/*
+ * Forward pass with P.V in fp8 (OCP e4m3), the FP8 PV variant of "Kernel
+ * Bottleneck Tuning (validated on FA4 FP4/FP8 PV, GB300)" (introduction and
+ * section 5). Q.K^T stays bf16. V arrives as e4m3 codes with one fp32 scale per
+ * head: V[t, h, :] = decode(v_e4m3[t, h, :]) * v_scale[h]. After exp2, P is
+ * rounded to e4m3 with a power-of-two scale folded into the exp2 argument (the
+ * log-domain refactoring of that page's section 4); the row sum uses the fp32
+ * values before rounding, and the epilogue folds v_scale and the inverse P
+ * scale into the single normalising multiply.
+ *   v_e4m3   uint8 [total_k, num_heads, head_dim], 16-byte aligned
+ *   v_scale  fp32 [num_heads] device array
+ * Every other argument as for fmha_fwd. head_dim must be 128.
+ */
+fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3,
+                             const float* v_scale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t total_q, int32_t total_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t num_heads, int32_t head_dim,
+                             int32_t causal, float softmax_scale,
+                             void* out, float* lse, void* stream);
+
+/*
+ * Host-side check of a cu_seqlens array (HOST pointer, batch + 1 entries):
+ * starts at 0, is non-decreasing, ends at total, and no document is longer
+ * than max_seqlen. Returns FMHA_OK or FMHA_ERR_INVALID_ARG. Makes no HIP call.
+ */
+fmha_status_t fmha_validate_cu_seqlens(const int32_t* host_cu_seqlens, int32_t batch,
+                                       int32_t total, int32_t max_seqlen);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fmha_status_string(fmha_status_t status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int32_t fmha_abi_version(void);
+
+#define FMHA_ABI_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMHA_H_ */

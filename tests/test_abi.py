@@ -1,0 +1,133 @@
+"""CPU tests of the C-ABI boundary: the library loads without a GPU, exports every
+function include/fmha.h declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmha.h")
+LIB = os.path.join(ROOT, "head_attention_forward_fmha_amd", "libfmha.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libfmha.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fmha_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(["fmha_fwd", "fmha_fwd_fp8pv", "fmha_validate_cu_seqlens",
+                            "fmha_status_string", "fmha_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(fm.EXPORTED_SYMBOLS) == set(_declared_functions())
+    assert fm.abi_version() == (1 << 16)
+
+
+def test_status_strings():
+    import head_attention_forward_fmha_amd as fm
+    assert fm.status_string(0) == "ok"
+    assert fm.status_string(1) == "invalid argument"
+    assert fm.status_string(2) == "unsupported configuration"
+    assert fm.status_string(3) == "kernel launch failed"
+    assert fm.status_string(99) == "unknown status"
+
+
+def _call_fwd(**kw):
+    """Call fmha_fwd with fake (never dereferenced) aligned pointers."""
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    a = dict(q=0x10000, k=0x20000, v=0x30000, cu_q=None, cu_k=None, batch=1, total_q=128,
+             total_k=128, max_q=128, max_k=128, heads=2, d=64, causal=0, scale=0.125,
+             out=0x40000, lse=0x50000)
+    a.update(kw)
+    return lib.fmha_fwd(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["batch"], a["total_q"],
+                        a["total_k"], a["max_q"], a["max_k"], a["heads"], a["d"], a["causal"],
+                        ctypes.c_float(a["scale"]), a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), 2),
+    (dict(d=256), 2),
+    (dict(heads=0), 1),
+    (dict(batch=-1), 1),
+    (dict(total_q=-5), 1),
+    (dict(causal=2), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1),
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(k=0x20008), 1),          # misaligned
+    (dict(lse=0x50002), 1),
+    (dict(total_q=100), 1),        # dense: total != batch * max_seqlen
+    (dict(cu_q=0x60000), 1),       # only one cu_seqlens pointer
+    (dict(heads=70000), 2),
+])
+def test_fwd_rejects_bad_arguments(kw, status):
+    assert _call_fwd(**kw) == status
+
+
+def test_fwd_empty_problem_is_a_no_op():
+    # no kernel is launched (so no GPU is needed) when there is nothing to compute
+    assert _call_fwd(batch=0, total_q=0, total_k=0, max_q=0, max_k=0, q=None, k=None, v=None,
+                     out=None, lse=None) == 0
+
+
+def test_fp8_rejects_head_dim_64_and_missing_scale():
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    args = [0x10000, 0x20000, 0x30000, 0x70000, None, None, 1, 128, 128, 128, 128, 2, 64, 0,
+            ctypes.c_float(0.125), 0x40000, 0x50000, None]
+    assert lib.fmha_fwd_fp8pv(*args) == 2
+    args[12] = 128
+    args[3] = None
+    assert lib.fmha_fwd_fp8pv(*args) == 1
+
+
+@pytest.mark.parametrize("cu,total,max_s,ok", [
+    ([0, 2048, 4096, 6144, 8192], 8192, 2048, True),
+    ([0, 2048, 4096, 6144, 8192], 8192, 2047, False),   # a doc longer than max_seqlen
+    ([0, 10, 5, 20], 20, 15, False),                     # decreasing
+    ([1, 10], 10, 10, False),                            # does not start at 0
+    ([0, 10], 11, 10, False),                            # does not end at total
+    ([0, 0, 0, 7], 7, 7, True),                          # empty documents are fine
+    ([0], 0, 0, True),
+])
+def test_validate_cu_seqlens(cu, total, max_s, ok):
+    import head_attention_forward_fmha_amd as fm
+    assert fm.validate_cu_seqlens(np.array(cu, np.int32), total, max_s) is ok
+
+
+def test_resource_gate_parser():
+    from head_attention_forward_fmha_amd.build import check_resources, parse_resource_report
+    text = ("remark: a.hip:1:0: Function Name: kern [-Rpass-analysis=kernel-resource-usage]\n"
+            "remark: a.hip:1:0:     VGPRs: 200 [-Rpass-analysis=kernel-resource-usage]\n"
+            "remark: a.hip:1:0:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]\n"
+            "remark: a.hip:1:0:     VGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]\n")
+    k = parse_resource_report(text)
+    assert k["kern"]["VGPRs"] == "200"
+    bad = check_resources(k)
+    assert len(bad) == 2
+
+
+def test_built_kernels_have_no_scratch_or_spills():
+    from head_attention_forward_fmha_amd.build import (RESOURCE_REPORT, check_resources,
+                                                       parse_resource_report)
+    if not os.path.exists(RESOURCE_REPORT):
+        pytest.skip("resource report not present (library built elsewhere)")
+    kernels = parse_resource_report(open(RESOURCE_REPORT).read())
+    assert any("fmha_fwd_kernel" in k for k in kernels)
+    assert check_resources(kernels) == []

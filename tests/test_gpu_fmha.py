@@ -1,0 +1,266 @@
+"""GPU parity of the HIP forward pass against the fp64 oracle, through the C ABI.
+
+Bar (bf16): |O_gpu - O_ref| <= 1e-2 + 1e-2 |O_ref| elementwise and
+|LSE_gpu - LSE_ref| <= 1e-3 on finite rows, -inf rows matching exactly.
+Bar (fp8 P.V): |O_gpu - O_ref| <= 5e-2 + 5e-2 |O_ref|, LSE as for bf16 (the row
+sum is taken before P is rounded to e4m3).
+
+The five workloads are checked at their full sizes in the launch configuration
+the benchmark times: the small ones on every output, the large ones on sampled
+(token, head) rows the oracle computes one by one (each from its complete score
+row). Edge cases cover ragged tails, empty documents, sq != sk with causal
+bottom-right alignment, d = 64, and tiny documents.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+O_ATOL = O_RTOL = 1e-2
+O_ATOL_FP8 = O_RTOL_FP8 = 5e-2
+LSE_ATOL = 1e-3
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _run(inp, causal, scale, heads, d, fp8=False, max_q=None, max_k=None):
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    q, k = inp.q.to(dev), inp.k.to(dev)
+    cq = torch.from_numpy(np.asarray(inp.cu_q, np.int32)).to(dev)
+    ck = torch.from_numpy(np.asarray(inp.cu_k, np.int32)).to(dev)
+    lq = np.diff(np.asarray(inp.cu_q))
+    lk = np.diff(np.asarray(inp.cu_k))
+    mq = int(lq.max()) if max_q is None else max_q
+    mk = int(lk.max()) if max_k is None else max_k
+    out = torch.full((q.shape[0], heads, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((heads, q.shape[0]), float("nan"), dtype=torch.float32, device=dev)
+    if fp8:
+        fm.fwd_fp8pv(q, k, inp.v_e4m3.to(dev), inp.v_scale.to(dev), cq, ck, mq, mk, causal=causal,
+                     softmax_scale=scale, out=out, lse=lse)
+    else:
+        fm.fwd(q, k, inp.v.to(dev), cq, ck, mq, mk, causal=causal, softmax_scale=scale, out=out,
+               lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(o, lse, o_ref, lse_ref, fp8=False, what=""):
+    atol, rtol = (O_ATOL_FP8, O_RTOL_FP8) if fp8 else (O_ATOL, O_RTOL)
+    assert not np.isnan(o).any(), f"{what}: NaN in O (unwritten or invalid output)"
+    err = np.abs(o - o_ref)
+    bad = err > atol + rtol * np.abs(o_ref)
+    if bad.any():
+        idx = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(o_ref))), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} O elements out of tolerance; worst at {idx}: "
+                             f"gpu {o[idx]} ref {o_ref[idx]} (max abs err {err.max():.3e})")
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isneginf(lse), ~fin), f"{what}: -inf LSE rows differ"
+    if fin.any():
+        lerr = np.abs(lse[fin] - lse_ref[fin])
+        assert lerr.max() <= LSE_ATOL, f"{what}: LSE max err {lerr.max():.3e}"
+
+
+def _full_parity(lens, heads, d, causal, seed=0, scale=None, fp8=False, max_q=None, max_k=None):
+    inp = make_inputs(lens, heads, d, seed=seed, fp8_pv=fp8)
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    o, lse = _run(inp, causal, scale, heads, d, fp8=fp8, max_q=max_q, max_k=max_k)
+    if fp8:
+        o_ref, lse_ref = oracle.attention_fp8pv(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                                inp.cu_k, causal, scale)
+    else:
+        o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
+    _check(o, lse, o_ref, lse_ref, fp8=fp8, what=f"lens={lens} h={heads} d={d} causal={causal}")
+    return inp, o, lse
+
+
+def _sample_rows(cu, heads, n_random, seed):
+    """(token, head) samples: tile-boundary rows of every document plus random rows."""
+    rng = np.random.default_rng(seed)
+    cu = np.asarray(cu, np.int64)
+    s = set()
+    for b in range(len(cu) - 1):
+        a, e = int(cu[b]), int(cu[b + 1])
+        for r in (0, 1, 31, 32, 63, 64, 127, 128, 129, e - a - 129, e - a - 2, e - a - 1):
+            if 0 <= r < e - a:
+                s.add((a + r, int(rng.integers(heads))))
+    for t in rng.integers(0, int(cu[-1]), n_random):
+        s.add((int(t), int(rng.integers(heads))))
+    return sorted(s)
+
+
+def _sampled_parity(w, n_random=1500, seed=0):
+    inp = workload_inputs(w)
+    o, lse = _run(inp, w.causal, w.softmax_scale, w.heads, w.head_dim, fp8=w.fp8_pv)
+    samples = _sample_rows(inp.cu_q, w.heads, n_random, seed)
+    if w.fp8_pv:
+        o_ref, l_ref = oracle.attention_fp8pv_sampled(inp.q, inp.k, inp.v_e4m3, inp.v_scale,
+                                                      inp.cu_q, inp.cu_k, w.causal,
+                                                      w.softmax_scale, samples)
+    else:
+        o_ref, l_ref = oracle.attention_sampled(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, w.causal,
+                                                w.softmax_scale, samples)
+    t = np.array([a for a, _ in samples])
+    hh = np.array([b for _, b in samples])
+    _check(o[t, hh], lse[hh, t], o_ref, l_ref, fp8=w.fp8_pv, what=w.name)
+    # every output element was written and finite
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    return o, lse
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_c1_tiny_dense_full():
+    w = WORKLOADS["c1_tiny_dense"]
+    inp = workload_inputs(w)
+    o, lse = _run(inp, w.causal, w.softmax_scale, w.heads, w.head_dim)
+    g = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                             "c1_tiny_dense_seed0.npz"), allow_pickle=False)
+    _check(o, lse, g["o"], g["lse"], what="c1")
+
+
+def test_c2_dense_2225_full():
+    w = WORKLOADS["c2_dense_2225"]
+    _full_parity(w.doc_lens, w.heads, w.head_dim, w.causal)
+
+
+def test_c2_dense_layout_matches_packed():
+    """The dense [b,s,h,d] call (no cu_seqlens) equals the packed call bitwise."""
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    inp = make_inputs(((300, 300), (300, 300)), 4, 128, seed=5)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq = torch.from_numpy(inp.cu_q).to(dev)
+    o1, l1 = fm.fwd(q, k, v, cq, cq, 300, 300)
+    o2, l2 = fm.fwd(q.view(2, 300, 4, 128), k.view(2, 300, 4, 128), v.view(2, 300, 4, 128))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(2, 300, 4, 128), o2)
+    assert torch.equal(l1, l2)
+
+
+def test_c3_varlen_causal_8k_sampled():
+    _sampled_parity(WORKLOADS["c3_varlen_causal_8k"])
+
+
+def test_c4_varlen_causal_32k_sampled():
+    _sampled_parity(WORKLOADS["c4_varlen_causal_32k"], n_random=1000)
+
+
+def test_c5_causal_fp8pv_32k_sampled():
+    _sampled_parity(WORKLOADS["c5_causal_fp8pv_32k"], n_random=600)
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("lens", [
+    ((1, 1),), ((63, 63),), ((65, 65),), ((127, 127),), ((129, 129),), ((200, 200),),
+    ((129, 129), (1, 1), (64, 64), (300, 300)),
+])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_lengths(lens, causal, d):
+    _full_parity(lens, 3, d, causal, seed=len(lens) + d)
+
+
+@pytest.mark.parametrize("lens", [
+    ((100, 300),), ((300, 100),), ((1, 129),), ((129, 1),), ((70, 0),), ((0, 50), (40, 40)),
+    ((5, 5), (0, 0), (130, 7), (7, 130)),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unequal_and_empty_documents(lens, causal):
+    _full_parity(lens, 2, 128, causal, seed=7)
+
+
+def test_many_small_documents():
+    rng = np.random.default_rng(3)
+    lens = tuple((int(x), int(x)) for x in rng.integers(0, 200, 40))
+    for causal in (False, True):
+        _full_parity(lens, 4, 128, causal, seed=11)
+
+
+def test_fp8_small_cases():
+    for lens, causal in ((((200, 200),), True), (((129, 129), (64, 64)), False),
+                         (((100, 300), (300, 100)), True)):
+        _full_parity(lens, 2, 128, causal, fp8=True, seed=13)
+
+
+def test_nonstandard_scale_and_large_scores():
+    # a large scale makes every row nearly one-hot: the max-subtraction must hold
+    _full_parity(((256, 256),), 2, 128, True, scale=1.0, seed=17)
+    _full_parity(((256, 256),), 2, 64, False, scale=0.5, seed=18)
+
+
+def test_max_seqlen_larger_than_needed():
+    # a generous max_seqlen only adds empty work items
+    _full_parity(((100, 100), (50, 50)), 2, 128, True, max_q=1000, max_k=1000, seed=19)
+
+
+# ---------------------------------------------------------------- bitwise properties
+
+def test_deterministic_repeats():
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    inp = make_inputs(((1000, 1000), (777, 777)), 8, 128, seed=21)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq = torch.from_numpy(inp.cu_q).to(dev)
+    ref_o, ref_l = fm.fwd(q, k, v, cq, cq, 1000, 1000, causal=True)
+    for _ in range(20):
+        o, l = fm.fwd(q, k, v, cq, cq, 1000, 1000, causal=True)
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_causal_future_keys_do_not_leak():
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    inp = make_inputs(((500, 500),), 4, 128, seed=23)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq = torch.from_numpy(inp.cu_q).to(dev)
+    o1, l1 = fm.fwd(q, k, v, cq, cq, 500, 500, causal=True)
+    i = 200
+    k2, v2 = k.clone(), v.clone()
+    k2[i + 1:] = k2[i + 1:] * 3 + 1
+    v2[i + 1:] = -v2[i + 1:]
+    o2, l2 = fm.fwd(q, k2, v2, cq, cq, 500, 500, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:i + 1], o2[:i + 1]) and torch.equal(l1[:, :i + 1], l2[:, :i + 1])
+    assert not torch.equal(o1[i + 1:], o2[i + 1:])
+
+
+def test_documents_are_isolated_and_match_per_document_calls():
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    lens = ((300, 300), (129, 129), (513, 513))
+    inp = make_inputs(lens, 4, 128, seed=25)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq = torch.from_numpy(inp.cu_q).to(dev)
+    o, l = fm.fwd(q, k, v, cq, cq, 513, 513, causal=True)
+    for b in range(3):
+        a, e = int(inp.cu_q[b]), int(inp.cu_q[b + 1])
+        ob, lb = fm.fwd(q[a:e].contiguous(), k[a:e].contiguous(), v[a:e].contiguous(), causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ob, o[a:e]) and torch.equal(lb, l[:, a:e])
+
+
+def test_causal_row0_is_v0_exactly():
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    inp = make_inputs(((64, 64), (200, 200)), 4, 128, seed=27)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq = torch.from_numpy(inp.cu_q).to(dev)
+    o, l = fm.fwd(q, k, v, cq, cq, 200, 200, causal=True)
+    torch.cuda.synchronize()
+    for a in (0, 64):
+        assert torch.equal(o[a], v[a])
+        ref = 0.08838834764831845 * (q[a].double().cpu() * k[a].double().cpu()).sum(-1)
+        assert torch.allclose(l[:, a].double().cpu(), ref, atol=1e-4, rtol=0)
