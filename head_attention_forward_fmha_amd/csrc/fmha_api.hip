@@ -38,7 +38,7 @@ fmha_status_t check_common(const void* q, const void* k, const void* v,
   const int64_t row = (int64_t)heads * head_dim;
   if (row * (int64_t)total_q > INT32_MAX || row * (int64_t)total_k > INT32_MAX ||
       (int64_t)heads * total_q > INT32_MAX || batch > 65535 || heads > 65535 ||
-      ((int64_t)max_q + 127) / 128 > 65535)
+      ((int64_t)max_q + 127) / 128 * heads * batch > INT32_MAX)
     return FMHA_ERR_UNSUPPORTED;
   if (total_q > 0 && (q == nullptr || out == nullptr)) return FMHA_ERR_INVALID_ARG;
   if (total_k > 0 && (k == nullptr || v == nullptr)) return FMHA_ERR_INVALID_ARG;

@@ -11,11 +11,11 @@
 // the Blackwell kernels those pages discuss.
 //
 // Work decomposition. One workgroup = 4 waves = 128 query rows of one
-// (document, head); each wave owns 32 query rows. The grid is
-// (heads, documents, query blocks) with the query-block index reversed, so the
-// longest causal blocks are dispatched first, and all blocks of one
-// (document, head) land on the same XCD whenever heads*documents is a
-// multiple of 8 (workgroups are dealt to the 8 XCDs round-robin).
+// (document, head); each wave owns 32 query rows. The 1-D grid is remapped so
+// that each XCD (workgroups are dealt to the 8 XCDs round-robin) runs one
+// contiguous range of (document, head) pairs with all their query blocks,
+// longest causal block first: the blocks that stream the same K/V run together
+// on one XCD and share its L2.
 //
 // Orientation. Both products are computed transposed so that every lane owns
 // one query column of the MFMA result:
@@ -32,8 +32,8 @@
 // K/V streaming. K and V tiles of 64 keys are copied HBM -> LDS with
 // global_load_lds_dwordx4 (no VGPR staging) into a double buffer; tile j+1 is
 // in flight while tile j is computed. Rows are XOR-swizzled in 16-byte chunks
-// (chunk c of row r is stored at c ^ (r mod chunks_per_row)) so that both the
-// 16-byte K reads and the 8-byte transposed V reads spread over the banks.
+// (see swz) so that both the 16-byte K reads and the 8-byte transposed V reads
+// spread over all 64 banks.
 // Key rows past the end of a document are clamped to its last row; their
 // scores are masked to -inf, so they contribute exactly zero.
 
@@ -52,6 +52,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLOBAL_AS __attribute__((address_space(1)))
@@ -60,6 +61,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per K/V tile
+constexpr int kXcds = 8;          // accelerator complex dies of an MI355X
 // fp8 P.V: P is quantised as e4m3(2^8 * p); 2^8 is the largest power of two
 // not above e4m3's maximum 448, so p = 1 maps exactly and small p stay normal.
 constexpr float kPScaleLog2 = 8.f;
@@ -90,17 +92,67 @@ __device__ __forceinline__ float wave_half_swap_sum(float x) {
   return lo + hi;
 }
 
+// Bank-spreading swizzle of 16-byte chunks: chunk c of row r is stored at
+// c ^ swz(r). The LDS has 64 4-byte banks (256 bytes). Requirements:
+//  * 16 consecutive rows read at one logical chunk (the 16-byte K operand
+//    reads) must land on 16 distinct bank groups;
+//  * the transposed V reads fetch 4 consecutive rows x 4 consecutive chunks
+//    (bf16) or 8 rows x 2 chunks (fp8) per half-wave, which must also be
+//    spread over all banks.
+// For 256-byte rows (16 chunks) the low two row bits select the high two chunk
+// bits; for 128-byte rows (8 chunks, two rows per bank sweep) row bit 1 selects
+// chunk bit 2 and row bits 2-3 the low two chunk bits.
+template <int kChunksPerRow>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(kChunksPerRow == 16 || kChunksPerRow == 8, "rows are 128 or 256 bytes");
+  if constexpr (kChunksPerRow == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory ops are in flight
 // (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
 // lgkmcnt left at their maxima so they are not waited on).
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt immediate that waits for all LDS/scalar-memory ops (lgkmcnt = 0)
+constexpr int waitcnt_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
-__device__ __forceinline__ void lds_dma_16(const void* gsrc, void* ldst) {
-  __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)gsrc, (LDS_AS void*)ldst, 16, 0, 0);
+// Buffer resource (V#) for raw byte-addressed loads: base, size in bytes, and
+// the gfx9 raw-buffer format word. Loads at offsets >= num_bytes return zero,
+// which is how rows past the end of a document are filled.
+__device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000;                                                  // 32-bit data format
+  return r;
 }
 
-// kFp8: V arrives as e4m3 codes and P.V runs on v_mfma_scale_f32_32x32x64_f8f6f4
-// (the FP8 PV variant of "Kernel Bottleneck Tuning"); Q.K^T stays bf16.
+// HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l
+// writes LDS bytes [lds + 16*l, lds + 16*l + 16). Written as inline asm so that
+// the compiler does not serialise it against unrelated LDS reads; the kernel
+// orders it explicitly with s_waitcnt vmcnt + s_barrier. m0 is reserved by the
+// compiler and never holds a live value in these kernels.
+__device__ __forceinline__ void lds_dma_16(uint32_t lds_addr, int voffset, i32x4 rsrc,
+                                           int soffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const LDS_AS char*)(const char*)p);
+}
+
+// Compiler-only fence: keeps LDS accesses on their side of a barrier.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 template <int kD, bool kCausal, bool kFp8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
@@ -123,9 +175,20 @@ void fmha_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_k[2][kTileBytes];   // [stage]
   __shared__ __attribute__((aligned(1024))) char smem_v[2][kVTileBytes];  // [stage]
 
-  const int head = blockIdx.x;
-  const int doc = blockIdx.y;
-  const int mblock = gridDim.z - 1 - blockIdx.z;
+  // ---- work item. Workgroups are dealt to the 8 XCDs round-robin (id % 8).
+  // Work items are ordered (document, head)-major with query blocks inner,
+  // longest (causal) block first, and each XCD takes one contiguous range of
+  // them, so the query blocks sharing one K/V stream run together on one XCD
+  // and hit in its L2.
+  const int n_items = p.batch * p.heads * p.n_mblocks;
+  const int wg = blockIdx.x;
+  const int xcd = wg % kXcds;
+  const int per = n_items / kXcds, extra = n_items % kXcds;
+  const int item = xcd * per + min(xcd, extra) + wg / kXcds;
+  const int pair = item / p.n_mblocks;
+  const int mblock = p.n_mblocks - 1 - (item - pair * p.n_mblocks);
+  const int doc = pair / p.heads;
+  const int head = pair - doc * p.heads;
 
   int q_start, q_end, k_start, k_end;
   if (p.cu_q != nullptr) {
@@ -165,52 +228,57 @@ void fmha_fwd_kernel(FwdParams p) {
     const bf16_t* qp = (const bf16_t*)p.q + (size_t)qrow * row_stride + head * kD + 8 * half;
 #pragma unroll
     for (int t = 0; t < kKSteps; ++t) qreg[t] = *(const bf16x8*)(qp + 16 * t);
+    // Q has landed before the K/V stream starts, so no wait on the stream's
+    // vector-memory counter is ever needed for Q inside the tile loop
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
 
-  // ---- per-lane constants of the HBM -> LDS copy
-  // Each wave copies 1 KB blocks: lane l lands at byte 16*l of the block, so
-  // the swizzle is applied by choosing which global chunk each lane fetches.
-  int ld_row[kLoadsPerWave];
-  int ld_col[kLoadsPerWave];  // byte offset of the logical 16-byte chunk in a K row
+  // ---- HBM -> LDS copy. Each wave copies 1 KB blocks: lane l lands at byte
+  // 16*l of the block, so the swizzle is applied by choosing which global chunk
+  // each lane fetches. Offsets are relative to this (document, head); rows past
+  // the document end fall outside the buffer and arrive as zeros.
+  const uint32_t k_stride = (uint32_t)p.heads * kRowBytes;   // bytes between K tokens
+  const uint32_t v_stride = (uint32_t)p.heads * kVRowBytes;  // bytes between V tokens
+  const i32x4 k_rsrc = make_buffer_rsrc(
+      (const char*)p.k + (size_t)k_start * k_stride + head * kRowBytes, (uint32_t)sk * k_stride);
+  const i32x4 v_rsrc = make_buffer_rsrc(
+      (const char*)p.v + (size_t)k_start * v_stride + head * kVRowBytes, (uint32_t)sk * v_stride);
+  int k_voff[kLoadsPerWave];
 #pragma unroll
   for (int r = 0; r < kLoadsPerWave; ++r) {
     const int byte = 1024 * (r * kWaves + wave) + 16 * lane;
     const int row = byte / kRowBytes;
     const int phys = (byte % kRowBytes) / 16;
-    ld_row[r] = row;
-    ld_col[r] = (phys ^ (row % kChunks)) * 16;
+    k_voff[r] = row * (int)k_stride + (phys ^ swz<kChunks>(row)) * 16;
   }
-  int lv_row[kVLoadsPerWave];
-  int lv_col[kVLoadsPerWave];  // byte offset of the logical 16-byte chunk in a V row
+  int v_voff[kVLoadsPerWave];
 #pragma unroll
   for (int r = 0; r < kVLoadsPerWave; ++r) {
     const int byte = 1024 * (r * kWaves + wave) + 16 * lane;
     const int row = byte / kVRowBytes;
     const int phys = (byte % kVRowBytes) / 16;
-    lv_row[r] = row;
-    lv_col[r] = (phys ^ (row % kVChunks)) * 16;
+    v_voff[r] = row * (int)v_stride + (phys ^ swz<kVChunks>(row)) * 16;
   }
-  const char* kbase = (const char*)p.k + head * kRowBytes;
-  const char* vbase = (const char*)p.v + head * kVRowBytes;
-  const size_t k_stride = (size_t)p.heads * kRowBytes;    // bytes between K tokens
-  const size_t v_stride = (size_t)p.heads * kVRowBytes;   // bytes between V tokens
+  const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * wave]);
+  const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * wave]);
 
   auto issue_tile = [&](int j, int stage) {
     const int kt0 = j * kBN;
 #pragma unroll
-    for (int r = 0; r < kLoadsPerWave; ++r) {
-      const int grow = k_start + min(kt0 + ld_row[r], sk - 1);
-      lds_dma_16(kbase + grow * k_stride + ld_col[r], &smem_k[stage][1024 * (r * kWaves + wave)]);
-    }
+    for (int r = 0; r < kLoadsPerWave; ++r)
+      lds_dma_16(k_lds0 + stage * kTileBytes + 1024 * kWaves * r, k_voff[r], k_rsrc,
+                 (int)((uint32_t)kt0 * k_stride));
 #pragma unroll
-    for (int r = 0; r < kVLoadsPerWave; ++r) {
-      const int grow = k_start + min(kt0 + lv_row[r], sk - 1);
-      lds_dma_16(vbase + grow * v_stride + lv_col[r], &smem_v[stage][1024 * (r * kWaves + wave)]);
-    }
+    for (int r = 0; r < kVLoadsPerWave; ++r)
+      lds_dma_16(v_lds0 + stage * kVTileBytes + 1024 * kWaves * r, v_voff[r], v_rsrc,
+                 (int)((uint32_t)kt0 * v_stride));
   };
 
   // ---- softmax state (per lane = per query; lanes n and n+32 agree)
   const float c = p.scale_log2;       // softmax_scale * log2(e)
+  // bf16 P tolerates p up to 2^8; e4m3 P already spends its range on the
+  // 2^kPScaleLog2 scale, so the fp8 path keeps the exact running maximum.
+  constexpr float kLazyLog2 = kFp8 ? 0.f : 8.f;
   float m_run = -__builtin_inff();    // running max of raw scores
   float l_run = 0.f;                  // running sum of exp2(c*(s - m_run))
   f32x16 oacc[kDBlocks];
@@ -223,6 +291,7 @@ void fmha_fwd_kernel(FwdParams p) {
 
   for (int j = 0; j < n_tiles; ++j) {
     const int stage = j & 1;
+    // tile j has landed once only tile j+1's copies can still be in flight
     if (j + 1 < n_tiles) {
       issue_tile(j + 1, stage ^ 1);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave + kVLoadsPerWave));
@@ -230,6 +299,7 @@ void fmha_fwd_kernel(FwdParams p) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
     __builtin_amdgcn_s_barrier();
+    compiler_fence();
 
     const int kt0 = j * kBN;
     // tiles entirely above the diagonal for all 32 rows of this wave are skipped
@@ -244,15 +314,23 @@ void fmha_fwd_kernel(FwdParams p) {
       for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int t = 0; t < kKSteps; ++t) {
+      // K operands for step t+1 are read while step t's MFMAs run
+      bf16x8 ka[2][kKeyBlocks];
+      auto read_k = [&](int t, bf16x8* dst) {
 #pragma unroll
         for (int kb = 0; kb < kKeyBlocks; ++kb) {
           const int row = 32 * kb + col;
-          const int chunk = (2 * t + half) ^ (row % kChunks);
-          const bf16x8 ka = *(const bf16x8*)(ks + row * kRowBytes + chunk * 16);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[t], sacc[kb], 0, 0, 0);
+          const int chunk = (2 * t + half) ^ swz<kChunks>(row);
+          dst[kb] = *(const bf16x8*)(ks + row * kRowBytes + chunk * 16);
         }
+      };
+      read_k(0, ka[0]);
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t) {
+        if (t + 1 < kKSteps) read_k(t + 1, ka[(t + 1) & 1]);
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t & 1][kb], qreg[t], sacc[kb], 0, 0, 0);
       }
 
       // ---- masking (only on the diagonal band and on the ragged key tail)
@@ -270,34 +348,47 @@ void fmha_fwd_kernel(FwdParams p) {
       }
 
       // ---- online softmax in the exp2 domain
-      float mx = -__builtin_inff();
+      // A row's maximum in use (m_run) is only raised when the row sees a
+      // score more than kLazyLog2 (base-2 units) above it; the O/l rescale pass
+      // then runs for the wave, with alpha = 1 exactly on rows that were not
+      // raised, so every row's arithmetic depends on its own scores only.
+      // Otherwise p = exp2(c*s - c*m_run) stays <= 2^kLazyLog2. Any m gives
+      // the same O and LSE in exact arithmetic; this only bounds p.
+      // four independent partial maxima keep the dependency chains short
+      float mp[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        for (int i = 0; i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], sacc[kb][i]);
+      float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
       mx = wave_half_swap_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      // fold: p = exp2(s*c - m_new*c); an all-masked row keeps the fold finite
-      const float neg_mc = (m_new == -__builtin_inff()) ? 0.f : -m_new * c;
-      const float alpha = __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, c, neg_mc));
-      // fp8: P is produced pre-multiplied by 2^kPScaleLog2 inside the exponent
+      // NaN when both are -inf (a row with nothing visible yet): no raise
+      const bool raise = (mx - m_run) * c > kLazyLog2;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        // raise implies mx > m_run and mx finite; alpha = 0 when m_run = -inf
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_run - mx) * c) : 1.f;
+        m_run = raise ? mx : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+      // fold: p = exp2(s*c - m_run*c); an all-masked row keeps the fold finite.
+      // fp8: P is produced pre-multiplied by 2^kPScaleLog2 inside the exponent.
+      const float neg_mc = (m_run == -__builtin_inff()) ? 0.f : -m_run * c;
       const float p_add = kFp8 ? neg_mc + kPScaleLog2 : neg_mc;
-      float rsum = 0.f;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, p_add));
           sacc[kb][i] = pv;
-          rsum += pv;
+          rs[i & 3] += pv;
         }
-      rsum = wave_half_swap_sum(rsum);
-      l_run = __builtin_fmaf(l_run, alpha, rsum);
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      // l_run holds this lane's half of the keys; the halves are added at the end
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
       const int g = lane >> 4;   // 16-lane group of the transposed reads
       const int gi = lane & 15;
@@ -318,7 +409,7 @@ void fmha_fwd_kernel(FwdParams p) {
             for (int r = 0; r < 2; ++r) {
               const int row = 16 * ks16 + 8 * r + 4 * half + gi / 4;
               const int d = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-              const int chunk = (d / 8) ^ (row % kVChunks);
+              const int chunk = (d / 8) ^ swz<kVChunks>(row);
               const char* addr = vs + row * kVRowBytes + chunk * 16 + (d % 8) * 2;
               va[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)addr);
             }
@@ -349,7 +440,7 @@ void fmha_fwd_kernel(FwdParams p) {
             const int e = gi >> 1;
             const int row = 32 * (r >> 1) + 16 * (r & 1) + 8 * (e >> 2) + 4 * half + (e & 3);
             const int byte_col = 32 * db + 16 * (g & 1) + 8 * (gi & 1);
-            const int chunk = (byte_col / 16) ^ (row % kVChunks);
+            const int chunk = (byte_col / 16) ^ swz<kVChunks>(row);
             const char* addr = vs + row * kVRowBytes + chunk * 16 + (byte_col % 16);
             const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)addr);
             a[2 * r] = t[0];
@@ -360,11 +451,14 @@ void fmha_fwd_kernel(FwdParams p) {
         }
       }
     }
-    // every wave is done reading this stage before it is refilled
+    // every wave's reads of this stage have returned before it is refilled
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     __builtin_amdgcn_s_barrier();
+    compiler_fence();
   }
 
   // ---- epilogue: O /= l, bf16 store; LSE = scale*m + ln(l)
+  l_run = wave_half_swap_sum(l_run);
   if (qi < sq) {
     // fp8: O = v_scale * sum(P_hat V_codes) / l, where l carries the same 2^kPScaleLog2
     const float num_scale = kFp8 ? p.v_scale[head] : 1.f;
@@ -392,10 +486,13 @@ void fmha_fwd_kernel(FwdParams p) {
 
 template <int kD, bool kCausal, bool kFp8>
 static hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  const int mblocks = (p.max_seqlen_q + kBM - 1) / kBM;
-  if (mblocks == 0 || p.batch == 0) return hipSuccess;
-  dim3 grid(p.heads, p.batch, mblocks);
-  hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kFp8>), grid, dim3(kThreads), 0, stream, p);
+  FwdParams q = p;
+  q.n_mblocks = (p.max_seqlen_q + kBM - 1) / kBM;
+  const long long n_items = (long long)q.n_mblocks * p.heads * p.batch;
+  if (n_items == 0) return hipSuccess;
+  if (n_items > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kFp8>), dim3((unsigned)n_items), dim3(kThreads),
+                     0, stream, q);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct FwdParams {
   int32_t max_seqlen_k;
   int32_t heads;
   float scale_log2;       // softmax_scale * log2(e)
+  int32_t n_mblocks;      // query blocks per document (set by the launcher)
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);

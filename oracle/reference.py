@@ -120,12 +120,11 @@ def attention(q, k, v, cu_seqlens_q: Sequence[int], cu_seqlens_k: Sequence[int],
     batch + 1. Returns (O [total_q, h, dv] fp64, LSE [h, total_q] fp64). Rows
     of documents or heads not selected (``heads``/``docs``) are NaN.
     """
-    qf, kf, vf = _as_f64(q), _as_f64(k), _as_f64(v)
     cq = np.asarray(cu_seqlens_q, dtype=np.int64)
     ck = np.asarray(cu_seqlens_k, dtype=np.int64)
     tau = float(np.float32(softmax_scale))
-    total_q, h, _ = qf.shape
-    dv = vf.shape[2]
+    total_q, h, _ = q.shape
+    dv = v.shape[2]
     out = np.full((total_q, h, dv), np.nan)
     lse = np.full((h, total_q), np.nan)
     head_list = range(h) if heads is None else list(heads)
@@ -134,11 +133,13 @@ def attention(q, k, v, cu_seqlens_q: Sequence[int], cu_seqlens_k: Sequence[int],
         q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
         sq = q1 - q0
         for hh in head_list:
-            kb, vb = kf[k0:k1, hh, :], vf[k0:k1, hh, :]
+            # widen only this (document, head) slice to fp64 (exact for bf16 inputs)
+            qb = _as_f64(q[q0:q1, hh, :])
+            kb, vb = _as_f64(k[k0:k1, hh, :]), _as_f64(v[k0:k1, hh, :])
             for r0 in range(0, sq, row_block):
                 r1 = min(sq, r0 + row_block)
                 rows = np.arange(r0, r1)
-                o, l = attention_rows(qf[q0 + r0:q0 + r1, hh, :], kb, vb, rows, sq, causal, tau)
+                o, l = attention_rows(qb[r0:r1], kb, vb, rows, sq, causal, tau)
                 out[q0 + r0:q0 + r1, hh, :] = o
                 lse[hh, q0 + r0:q0 + r1] = l
     return out, lse
