@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fmha_kernel_params.h"
 
 namespace fmha {
@@ -287,10 +289,41 @@ void fmha_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  if (n_tiles > 0) issue_tile(0, 0);
+  // ---- per-lane LDS byte offsets of the MFMA operand reads, relative to a
+  // stage's tile. Everything else in an address (stage, key block, 16-key step)
+  // is a compile-time immediate, because the swizzle only looks at the low four
+  // row bits and the stage is static in the unrolled loop below.
+  const int g = lane >> 4;   // 16-lane group of the transposed reads
+  const int gi = lane & 15;
+  int k_off[kKSteps];        // K rows 32*kb + col, logical chunk 2t + half
+#pragma unroll
+  for (int t = 0; t < kKSteps; ++t)
+    k_off[t] = col * kRowBytes + (((2 * t + half) ^ swz<kChunks>(col)) * 16);
+  // bf16 V (tr16): rows 16*ks16 + 8r + 4*half + gi/4, d = 32*db + 16*(g&1) + 4*(gi&3)
+  // fp8 V (tr8): rows 32*(r>>1) + 16*(r&1) + 8*(e>>2) + 4*half + (e&3), e = gi/2,
+  //              byte column 32*db + 16*(g&1) + 8*(gi&1)
+  constexpr int kVReads = kFp8 ? 1 : 2;
+  int v_off[kVReads][kDBlocks];
+#pragma unroll
+  for (int r = 0; r < kVReads; ++r)
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db) {
+      if constexpr (!kFp8) {
+        const int row = 8 * r + 4 * half + gi / 4;
+        const int d = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+        v_off[r][db] = row * kVRowBytes + (((d / 8) ^ swz<kVChunks>(row)) * 16) + (d % 8) * 2;
+      } else {
+        const int e = gi >> 1;
+        const int row = 8 * (e >> 2) + 4 * half + (e & 3);
+        const int byte_col = 32 * db + 16 * (g & 1) + 8 * (gi & 1);
+        v_off[r][db] =
+            row * kVRowBytes + (((byte_col / 16) ^ swz<kVChunks>(row)) * 16) + (byte_col % 16);
+      }
+    }
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
+  // ---- one K/V tile: wait for it, S^T = K Q^T, mask, online softmax, O^T += V^T P^T
+  auto step = [&](int j, auto stage_tag) {
+    constexpr int stage = decltype(stage_tag)::value;
     // tile j has landed once only tile j+1's copies can still be in flight
     if (j + 1 < n_tiles) {
       issue_tile(j + 1, stage ^ 1);
@@ -318,11 +351,8 @@ void fmha_fwd_kernel(FwdParams p) {
       bf16x8 ka[2][kKeyBlocks];
       auto read_k = [&](int t, bf16x8* dst) {
 #pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb) {
-          const int row = 32 * kb + col;
-          const int chunk = (2 * t + half) ^ swz<kChunks>(row);
-          dst[kb] = *(const bf16x8*)(ks + row * kRowBytes + chunk * 16);
-        }
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+          dst[kb] = *(const bf16x8*)(ks + k_off[t] + kb * 32 * kRowBytes);
       };
       read_k(0, ka[0]);
 #pragma unroll
@@ -354,7 +384,7 @@ void fmha_fwd_kernel(FwdParams p) {
       // raised, so every row's arithmetic depends on its own scores only.
       // Otherwise p = exp2(c*s - c*m_run) stays <= 2^kLazyLog2. Any m gives
       // the same O and LSE in exact arithmetic; this only bounds p.
-      // four independent partial maxima keep the dependency chains short
+      // Four independent partial maxima keep the dependency chains short.
       float mp[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb)
@@ -378,46 +408,47 @@ void fmha_fwd_kernel(FwdParams p) {
       // fp8: P is produced pre-multiplied by 2^kPScaleLog2 inside the exponent.
       const float neg_mc = (m_run == -__builtin_inff()) ? 0.f : -m_run * c;
       const float p_add = kFp8 ? neg_mc + kPScaleLog2 : neg_mc;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, p_add));
-          sacc[kb][i] = pv;
-          rs[i & 3] += pv;
-        }
-      // l_run holds this lane's half of the keys; the halves are added at the end
-      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        for (int i = 0; i < 16; ++i)
+          sacc[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, p_add));
 
-      const int g = lane >> 4;   // 16-lane group of the transposed reads
-      const int gi = lane & 15;
+      // row sum from the fp32 values, four independent chains; l_run holds this
+      // lane's half of the keys and the halves are added at the end
+      {
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) rs[i & 3] += sacc[kb][i];
+        l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      }
+
       if constexpr (!kFp8) {
-        // ---- O^T += V^T P^T, 16 keys per MFMA
+        // P in bf16 (round to nearest even) as the P.V operand
+        bf16x8 pb[kBN / 16];
 #pragma unroll
-        for (int ks16 = 0; ks16 < kBN / 16; ++ks16) {
-          const int kb = ks16 / 2, t = ks16 % 2;
-          bf16x8 pb;
+        for (int ks16 = 0; ks16 < kBN / 16; ++ks16)
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) pb[jj] = (bf16_t)sacc[kb][8 * t + jj];
+          for (int jj = 0; jj < 8; ++jj) pb[ks16][jj] = (bf16_t)sacc[ks16 / 2][8 * (ks16 % 2) + jj];
+
+        // ---- O^T += V^T P^T, 16 keys per MFMA. Lane (half, m) needs
+        // V[keys 16*ks16 + 8r + 4*half + 0..3][d = 32*db + m]; source lane gi of
+        // group g reads 4 d-values of key row (.. + gi/4).
+#pragma unroll
+        for (int ks16 = 0; ks16 < kBN / 16; ++ks16)
 #pragma unroll
           for (int db = 0; db < kDBlocks; ++db) {
-            // lane (half, m) needs V[keys 16*ks16 + 8r + 4*half + 0..3][d = 32*db + m]:
-            // source lane gi of group g reads 4 d-values of key row (.. + gi/4)
             bf16x4 va[2];
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-              const int row = 16 * ks16 + 8 * r + 4 * half + gi / 4;
-              const int d = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-              const int chunk = (d / 8) ^ swz<kVChunks>(row);
-              const char* addr = vs + row * kVRowBytes + chunk * 16 + (d % 8) * 2;
-              va[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)addr);
-            }
+            for (int r = 0; r < 2; ++r)
+              va[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (LDS_AS bf16x4*)(vs + v_off[r][db] + 16 * ks16 * kVRowBytes));
             const bf16x8 a = {va[0][0], va[0][1], va[0][2], va[0][3],
                               va[1][0], va[1][1], va[1][2], va[1][3]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks16], oacc[db], 0, 0, 0);
           }
-        }
       } else {
         // ---- O^T += V^T P^T in e4m3, all 64 keys of the tile in one MFMA per d block.
         // Byte j of a lane's operand is key kappa(half, j) =
@@ -436,13 +467,9 @@ void fmha_fwd_kernel(FwdParams p) {
           i32x8 a;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            // read r delivers bytes 8r..8r+7: keys of row e = gi/2 of this read
-            const int e = gi >> 1;
-            const int row = 32 * (r >> 1) + 16 * (r & 1) + 8 * (e >> 2) + 4 * half + (e & 3);
-            const int byte_col = 32 * db + 16 * (g & 1) + 8 * (gi & 1);
-            const int chunk = (byte_col / 16) ^ swz<kVChunks>(row);
-            const char* addr = vs + row * kVRowBytes + chunk * 16 + (byte_col % 16);
-            const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)addr);
+            // read r delivers bytes 8r..8r+7: keys 32*(r>>1) + 16*(r&1) + ...
+            const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (LDS_AS i32x2*)(vs + v_off[0][db] + (32 * (r >> 1) + 16 * (r & 1)) * kVRowBytes));
             a[2 * r] = t[0];
             a[2 * r + 1] = t[1];
           }
@@ -455,7 +482,15 @@ void fmha_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     __builtin_amdgcn_s_barrier();
     compiler_fence();
+  };
+
+  if (n_tiles > 0) issue_tile(0, 0);
+  int j = 0;
+  for (; j + 2 <= n_tiles; j += 2) {
+    step(j, std::integral_constant<int, 0>());
+    step(j + 1, std::integral_constant<int, 1>());
   }
+  if (j < n_tiles) step(j, std::integral_constant<int, 0>());
 
   // ---- epilogue: O /= l, bf16 store; LSE = scale*m + ln(l)
   l_run = wave_half_swap_sum(l_run);
