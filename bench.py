@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=sorted(SHORT) + sorted(SHORT.values()))
+    ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong"],
+                    help="kernel variant (auto picks by problem size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=16)
     ap.add_argument("--counters", action="store_true",
@@ -81,18 +83,18 @@ def device_inputs(w, dev):
     return inp, d
 
 
-def make_step(w, d):
+def make_step(w, d, variant="auto"):
     import head_attention_forward_fmha_amd as fm
     mq, mk = w.max_seqlen_q, w.max_seqlen_k
     if w.fp8_pv:
         def step():
             fm.fwd_fp8pv(d["q"], d["k"], d["v8"], d["vs"], d["cu_q"], d["cu_k"], mq, mk,
                          causal=w.causal, softmax_scale=w.softmax_scale, out=d["out"],
-                         lse=d["lse"])
+                         lse=d["lse"], variant=variant)
     else:
         def step():
             fm.fwd(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], mq, mk, causal=w.causal,
-                   softmax_scale=w.softmax_scale, out=d["out"], lse=d["lse"])
+                   softmax_scale=w.softmax_scale, out=d["out"], lse=d["lse"], variant=variant)
     return step
 
 
@@ -194,7 +196,7 @@ def main():
     w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     inp, d = device_inputs(w, dev)
-    step = make_step(w, d)
+    step = make_step(w, d, args.variant)
     if args.counters:
         run_counters(w, d, step)
         return
@@ -224,7 +226,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.description, "name": w.name, "total_tokens": w.total_q,
                    "docs": w.batch, "heads": w.heads, "head_dim": w.head_dim,
-                   "causal": w.causal, "seed": w.seed, "fp8_pv": w.fp8_pv},
+                   "causal": w.causal, "seed": w.seed, "fp8_pv": w.fp8_pv,
+                   "kernel_variant": args.variant},
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -19,10 +19,10 @@ import math
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import FMHA_OK, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
+from ._lib import FMHA_OK, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
 
 __all__ = ["fwd", "fwd_fp8pv", "validate_cu_seqlens", "status_string", "abi_version",
-           "FmhaError", "EXPORTED_SYMBOLS", "load_library"]
+           "FmhaError", "EXPORTED_SYMBOLS", "VARIANTS", "load_library"]
 
 
 def load_library():
@@ -96,11 +96,12 @@ def _stream_handle(device) -> int:
 def fwd(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[int] = None,
         max_seqlen_k: Optional[int] = None, causal: bool = False,
         softmax_scale: Optional[float] = None, out=None, lse=None,
-        return_lse: bool = True) -> Tuple:
+        return_lse: bool = True, variant: str = "auto") -> Tuple:
     """bf16 FMHA forward. Returns (out, lse) with lse fp32 [heads, total_q].
 
     q [total_q, h, d] / k, v [total_k, h, d] with cu_seqlens (int32 [batch+1]),
     or dense q [b, sq, h, d] / k, v [b, sk, h, d]. d must be 64 or 128.
+    variant: "auto", "four_wave" or "pingpong" (kernel choice; same function).
     """
     import torch
     lib = _lib.load()
@@ -116,10 +117,11 @@ def fwd(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[in
         out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
     if lse is None and return_lse:
         lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
-    st = lib.fmha_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"],
-                      s["total_q"], s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"],
-                      int(bool(causal)), ctypes.c_float(scale), _ptr(out), _ptr(lse),
-                      ctypes.c_void_p(_stream_handle(dev)))
+    st = lib.fmha_fwd_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(s["cu_q"]), _ptr(s["cu_k"]),
+                              s["batch"], s["total_q"], s["total_k"], s["max_q"], s["max_k"],
+                              s["heads"], s["d"], int(bool(causal)), ctypes.c_float(scale),
+                              _ptr(out), _ptr(lse), VARIANTS[variant],
+                              ctypes.c_void_p(_stream_handle(dev)))
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_fwd")
     return out, lse
@@ -128,7 +130,7 @@ def fwd(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[in
 def fwd_fp8pv(q, k, v_e4m3, v_scale, cu_seqlens_q=None, cu_seqlens_k=None,
               max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
               causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse=None,
-              return_lse: bool = True) -> Tuple:
+              return_lse: bool = True, variant: str = "auto") -> Tuple:
     """FMHA forward with P.V in fp8 e4m3. v_e4m3 is uint8 codes, v_scale fp32 [heads]."""
     import torch
     lib = _lib.load()
@@ -145,11 +147,12 @@ def fwd_fp8pv(q, k, v_e4m3, v_scale, cu_seqlens_q=None, cu_seqlens_k=None,
         out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
     if lse is None and return_lse:
         lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
-    st = lib.fmha_fwd_fp8pv(_ptr(q), _ptr(k), _ptr(v_e4m3), _ptr(v_scale), _ptr(s["cu_q"]),
-                            _ptr(s["cu_k"]), s["batch"], s["total_q"], s["total_k"], s["max_q"],
-                            s["max_k"], s["heads"], s["d"], int(bool(causal)),
-                            ctypes.c_float(scale), _ptr(out), _ptr(lse),
-                            ctypes.c_void_p(_stream_handle(dev)))
+    st = lib.fmha_fwd_fp8pv_variant(_ptr(q), _ptr(k), _ptr(v_e4m3), _ptr(v_scale),
+                                    _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"], s["total_q"],
+                                    s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"],
+                                    int(bool(causal)), ctypes.c_float(scale), _ptr(out),
+                                    _ptr(lse), VARIANTS[variant],
+                                    ctypes.c_void_p(_stream_handle(dev)))
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_fwd_fp8pv")
     return out, lse

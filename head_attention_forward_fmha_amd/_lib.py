@@ -18,9 +18,13 @@ FMHA_ERR_INVALID_ARG = 1
 FMHA_ERR_UNSUPPORTED = 2
 FMHA_ERR_LAUNCH = 3
 
+VARIANTS = {"auto": 0, "four_wave": 1, "pingpong": 2}
+
 EXPORTED_SYMBOLS = (
     "fmha_fwd",
     "fmha_fwd_fp8pv",
+    "fmha_fwd_variant",
+    "fmha_fwd_fp8pv_variant",
     "fmha_validate_cu_seqlens",
     "fmha_status_string",
     "fmha_abi_version",
@@ -68,6 +72,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmha_fwd.restype = ctypes.c_int
     lib.fmha_fwd_fp8pv.argtypes = _FWD_FP8_ARGS
     lib.fmha_fwd_fp8pv.restype = ctypes.c_int
+    lib.fmha_fwd_variant.argtypes = _FWD_ARGS[:-1] + [_i32, _vp]
+    lib.fmha_fwd_variant.restype = ctypes.c_int
+    lib.fmha_fwd_fp8pv_variant.argtypes = _FWD_FP8_ARGS[:-1] + [_i32, _vp]
+    lib.fmha_fwd_fp8pv_variant.restype = ctypes.c_int
     lib.fmha_validate_cu_seqlens.argtypes = [_vp, _i32, _i32, _i32]
     lib.fmha_validate_cu_seqlens.restype = ctypes.c_int
     lib.fmha_status_string.argtypes = [ctypes.c_int]

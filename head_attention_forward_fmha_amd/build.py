@@ -52,15 +52,20 @@ def _torch_lib_dir():
 
 
 def parse_resource_report(text: str) -> dict:
-    """Map kernel name -> {field: value} from clang's kernel-resource-usage remarks."""
+    """Map kernel name -> {field: value} from clang's kernel-resource-usage remarks.
+
+    The remarks look like
+      <file>:<line>:<col>: remark: Function Name: <symbol> [-Rpass-analysis=...]
+      <file>:<line>:<col>: remark:     VGPRs Spill: 0 [-Rpass-analysis=...]
+    """
     kernels = {}
     cur = None
     for line in text.splitlines():
-        m = re.search(r"Function Name: (\S+)", line)
+        m = re.search(r"remark:\s+Function Name:\s+(\S+)", line)
         if m:
             cur = kernels.setdefault(m.group(1), {})
             continue
-        m = re.search(r"remark: .*?:\s+([A-Za-z][A-Za-z /\[\]]*?):\s+(\S+) \[-Rpass", line)
+        m = re.search(r"remark:\s+([A-Za-z][A-Za-z /\[\]]*?):\s+(\S+)\s+\[-Rpass", line)
         if m and cur is not None:
             cur[m.group(1).strip()] = m.group(2)
     return kernels
@@ -70,6 +75,9 @@ def check_resources(kernels: dict) -> list:
     """Return a list of violations (scratch use or spills) in a parsed report."""
     bad = []
     for name, f in kernels.items():
+        if "ScratchSize [bytes/lane]" not in f or "VGPRs Spill" not in f:
+            bad.append(f"{name}: resource report incomplete ({sorted(f)})")
+            continue
         if f.get("ScratchSize [bytes/lane]", "0") != "0":
             bad.append(f"{name}: scratch {f.get('ScratchSize [bytes/lane]')} B/lane")
         for key in ("VGPRs Spill", "SGPRs Spill"):

@@ -75,6 +75,25 @@ fmha::FwdParams make_params(const void* q, const void* k, const void* v, const i
 
 extern "C" {
 
+fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads, int32_t head_dim,
+                               int32_t causal, float softmax_scale,
+                               void* out, float* lse, int32_t variant, void* stream) {
+  fmha_status_t st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
+                                  softmax_scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PINGPONG) return FMHA_ERR_INVALID_ARG;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
+  fmha::FwdParams p = make_params(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, softmax_scale, out, lse);
+  hipError_t e = fmha::launch_fwd_bf16(p, head_dim, causal != 0, variant, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
 fmha_status_t fmha_fwd(const void* q, const void* k, const void* v,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                        int32_t batch, int32_t total_q, int32_t total_k,
@@ -82,14 +101,33 @@ fmha_status_t fmha_fwd(const void* q, const void* k, const void* v,
                        int32_t num_heads, int32_t head_dim,
                        int32_t causal, float softmax_scale,
                        void* out, float* lse, void* stream) {
-  fmha_status_t st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
-                                  max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
-                                  softmax_scale, out, lse);
+  return fmha_fwd_variant(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                          max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal, softmax_scale,
+                          out, lse, FMHA_VARIANT_AUTO, stream);
+}
+
+fmha_status_t fmha_fwd_fp8pv_variant(const void* q, const void* k, const uint8_t* v_e4m3,
+                                     const float* v_scale,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t total_q, int32_t total_k,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_heads, int32_t head_dim,
+                                     int32_t causal, float softmax_scale,
+                                     void* out, float* lse, int32_t variant, void* stream) {
+  fmha_status_t st = check_common(q, k, v_e4m3, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim,
+                                  causal, softmax_scale, out, lse);
   if (st != FMHA_OK) return st;
+  if (head_dim != 128) return FMHA_ERR_UNSUPPORTED;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PINGPONG) return FMHA_ERR_INVALID_ARG;
+  if (total_k > 0 && v_scale == nullptr) return FMHA_ERR_INVALID_ARG;
+  if (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u)) return FMHA_ERR_INVALID_ARG;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
-  fmha::FwdParams p = make_params(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
-                                  max_seqlen_q, max_seqlen_k, num_heads, softmax_scale, out, lse);
-  hipError_t e = fmha::launch_fwd_bf16(p, head_dim, causal != 0, (hipStream_t)stream);
+  fmha::FwdParams p = make_params(q, k, v_e4m3, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, softmax_scale,
+                                  out, lse);
+  p.v_scale = v_scale;
+  hipError_t e = fmha::launch_fwd_fp8pv(p, head_dim, causal != 0, variant, (hipStream_t)stream);
   return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
 
@@ -101,20 +139,10 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
                              int32_t num_heads, int32_t head_dim,
                              int32_t causal, float softmax_scale,
                              void* out, float* lse, void* stream) {
-  fmha_status_t st = check_common(q, k, v_e4m3, cu_seqlens_q, cu_seqlens_k, batch, total_q,
-                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim,
-                                  causal, softmax_scale, out, lse);
-  if (st != FMHA_OK) return st;
-  if (head_dim != 128) return FMHA_ERR_UNSUPPORTED;
-  if (total_k > 0 && v_scale == nullptr) return FMHA_ERR_INVALID_ARG;
-  if (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u)) return FMHA_ERR_INVALID_ARG;
-  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
-  fmha::FwdParams p = make_params(q, k, v_e4m3, cu_seqlens_q, cu_seqlens_k, batch, total_q,
-                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, softmax_scale,
-                                  out, lse);
-  p.v_scale = v_scale;
-  hipError_t e = fmha::launch_fwd_fp8pv(p, head_dim, causal != 0, (hipStream_t)stream);
-  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+  return fmha_fwd_fp8pv_variant(q, k, v_e4m3, v_scale, cu_seqlens_q, cu_seqlens_k, batch,
+                                total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads,
+                                head_dim, causal, softmax_scale, out, lse, FMHA_VARIANT_AUTO,
+                                stream);
 }
 
 fmha_status_t fmha_validate_cu_seqlens(const int32_t* host_cu, int32_t batch, int32_t total,

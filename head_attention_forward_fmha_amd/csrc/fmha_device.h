@@ -1,0 +1,624 @@
+// Device-side building blocks of the gfx950 FMHA forward kernels.
+//
+// The operation (pages: "[BUG] Unexpected Slower Performance in C++ CuTe
+// (77_blackwell_fmha) vs Python CuTe DSL (fmha.py) on Jetson Thor", Key
+// Observation 2, the softmax_step listings; "Kernel Bottleneck Tuning",
+// section 4): per document and head, S = scale * Q K^T, an online softmax in
+// the exp2 domain with the scale and the running row maximum folded into one
+// fused multiply-add, P.V with fp32 accumulation, and an epilogue that
+// normalises O and writes LSE.
+//
+// Orientation. Both products are computed transposed so that every lane owns
+// one query column of the MFMA result:
+//   S^T[key, query] = K . Q^T   (v_mfma_f32_32x32x16_bf16, A = K rows from
+//                                LDS, B = Q held in registers)
+//   O^T[d, query]  += V^T . P^T (A = V read from LDS with ds_read_b64_tr_b16,
+//                                or _tr_b8 for e4m3 V; B = P straight from the
+//                                S^T accumulators)
+// A lane (half = lane/32, column n = lane%32) holds 16 keys of each 32-key S^T
+// block for query n: keys 8*(i/4) + 4*half + i%4 of accumulator register i.
+// The row max and row sum are in-lane reductions plus one v_permlane32_swap
+// between lanes n and n+32, and the online-softmax rescale of O is a per-lane
+// scalar. The transposed V reads fetch exactly the key order in which P leaves
+// the accumulator.
+//
+// LDS layout. K and V tiles are row-major [key][d] with 16-byte chunks
+// XOR-swizzled per row (swz) so that the 16-byte K operand reads and the 8-byte
+// transposed V reads both spread over all 64 banks. Tiles are copied
+// HBM -> LDS by buffer_load_dwordx4 ... lds, which needs no VGPR staging and
+// returns zeros for rows past the end of a document.
+
+#ifndef FMHA_DEVICE_H_
+#define FMHA_DEVICE_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "fmha_kernel_params.h"
+
+namespace fmha {
+
+typedef __bf16 bf16_t;
+typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16_t bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kBN = 64;     // keys per K/V tile
+constexpr int kXcds = 8;    // accelerator complex dies of an MI355X
+// fp8 P.V: P is quantised as e4m3(2^8 * p); 2^8 is the largest power of two
+// not above e4m3's maximum 448, so p = 1 maps exactly and small p stay normal.
+constexpr float kPScaleLog2 = 8.f;
+
+// ---------------------------------------------------------------- primitives
+
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second. With both operands holding x, the two results are
+// [x_lo, x_lo] and [x_hi, x_hi], so combining them all-reduces lanes n, n+32.
+// The results pass through an empty asm: without it the optimiser folds
+// fmaxf/fadd of the two float results into the first result alone.
+__device__ __forceinline__ void half_swap(float x, float& lo, float& hi) {
+  const int a = __builtin_bit_cast(int, x);
+  auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  int r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  lo = __builtin_bit_cast(float, r0);
+  hi = __builtin_bit_cast(float, r1);
+}
+
+__device__ __forceinline__ float wave_half_swap_max(float x) {
+  float lo, hi;
+  half_swap(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+
+__device__ __forceinline__ float wave_half_swap_sum(float x) {
+  float lo, hi;
+  half_swap(x, lo, hi);
+  return lo + hi;
+}
+
+// Bank-spreading swizzle of 16-byte chunks: chunk c of row r is stored at
+// c ^ swz(r). The LDS has 64 4-byte banks (256 bytes). Requirements:
+//  * 16 consecutive rows read at one logical chunk (the 16-byte K operand
+//    reads) must land on 16 distinct bank groups;
+//  * the transposed V reads fetch 4 consecutive rows x 4 consecutive chunks
+//    (bf16) or 8 rows x 2 chunks (fp8) per half-wave, which must also be
+//    spread over all banks.
+// For 256-byte rows (16 chunks) the low two row bits select the high two chunk
+// bits; for 128-byte rows (8 chunks, two rows per bank sweep) row bit 1 selects
+// chunk bit 2 and row bits 2-3 the low two chunk bits. Only the low four row
+// bits matter, so the swizzle repeats every 16 rows.
+template <int kChunksPerRow>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(kChunksPerRow == 16 || kChunksPerRow == 8, "rows are 128 or 256 bytes");
+  if constexpr (kChunksPerRow == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory ops are in flight
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
+// lgkmcnt left at their maxima so they are not waited on).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt immediate that waits for all LDS/scalar-memory ops (lgkmcnt = 0)
+constexpr int waitcnt_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
+
+// Buffer resource (V#) for raw byte-addressed loads: base, size in bytes, and
+// the gfx9 raw-buffer format word. Loads at offsets >= num_bytes return zero,
+// which is how rows past the end of a document are filled.
+__device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000;                                                  // 32-bit data format
+  return r;
+}
+
+// HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l
+// writes LDS bytes [lds + 16*l, lds + 16*l + 16). Written as inline asm so that
+// the compiler does not serialise it against unrelated LDS reads; the kernels
+// order it explicitly with s_waitcnt vmcnt + s_barrier. m0 is reserved by the
+// compiler and never holds a live value in these kernels.
+template <int kLdsOffset>
+__device__ __forceinline__ void lds_dma_16(uint32_t lds_base, int voffset, i32x4 rsrc,
+                                           int soffset) {
+  // m0 = lds_base + kLdsOffset is formed here, so that only the base stays live
+  // in a scalar register across the loop
+  asm volatile(
+      "s_add_u32 m0, %0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset), "n"(kLdsOffset)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const LDS_AS char*)(const char*)p);
+}
+
+// Compiler-only fence: keeps LDS accesses on their side of a barrier.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>()), ...);
+  }(std::make_integer_sequence<int, N>());
+}
+
+// Wait for every outstanding LDS read, then the workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// ---------------------------------------------------------------- work items
+
+struct WorkItem {
+  int head, q_start, k_start, sq, sk, m0;
+};
+
+// Workgroups are dealt to the 8 XCDs round-robin (id % 8). Work items are
+// ordered (document, head)-major with query blocks inner, longest causal block
+// first, and each XCD takes one contiguous range of them, so the query blocks
+// that stream the same K/V run together on one XCD and share its L2.
+__device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int bm) {
+  const int n_items = p.batch * p.heads * p.n_mblocks;
+  const int wg = blockIdx.x;
+  const int xcd = wg % kXcds;
+  const int per = n_items / kXcds, extra = n_items % kXcds;
+  const int item = xcd * per + min(xcd, extra) + wg / kXcds;
+  const int pair = item / p.n_mblocks;
+  const int mblock = p.n_mblocks - 1 - (item - pair * p.n_mblocks);
+  const int doc = pair / p.heads;
+  WorkItem w;
+  w.head = pair - doc * p.heads;
+  int q_end, k_end;
+  if (p.cu_q != nullptr) {
+    w.q_start = p.cu_q[doc];
+    q_end = p.cu_q[doc + 1];
+    w.k_start = p.cu_k[doc];
+    k_end = p.cu_k[doc + 1];
+  } else {
+    w.q_start = doc * p.max_seqlen_q;
+    q_end = w.q_start + p.max_seqlen_q;
+    w.k_start = doc * p.max_seqlen_k;
+    k_end = w.k_start + p.max_seqlen_k;
+  }
+  w.sq = q_end - w.q_start;
+  w.sk = k_end - w.k_start;
+  w.m0 = mblock * bm;
+  return w;
+}
+
+// ---------------------------------------------------------------- per-wave tile math
+
+// One wave's view of the forward pass: 32 query rows, Q in registers, the
+// running softmax state and the O^T accumulators. kWaves is the workgroup's
+// wave count (it sets how the K/V copies are split among the waves).
+template <int kD, bool kCausal, bool kFp8, int kWaves>
+struct WaveTile {
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRowBytes = kD * 2;               // one K row in bytes
+  static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per K row
+  static constexpr int kTileBytes = kBN * kRowBytes;     // one K tile
+  static constexpr int kLoadsPerWave = kTileBytes / (kThreads * 16);
+  static constexpr int kVRowBytes = kFp8 ? kD : kD * 2;  // one V row in bytes
+  static constexpr int kVChunks = kVRowBytes / 16;
+  static constexpr int kVTileBytes = kBN * kVRowBytes;
+  static constexpr int kVLoadsPerWave = kVTileBytes / (kThreads * 16);
+  static constexpr int kKSteps = kD / 16;                // QK^T MFMA steps over d
+  static constexpr int kDBlocks = kD / 32;               // O^T accumulator blocks
+  static constexpr int kKeyBlocks = kBN / 32;            // S^T accumulator blocks
+  static constexpr int kVReads = kFp8 ? 1 : 2;
+  // bf16 P tolerates p up to 2^8 (lazy maximum); e4m3 P already spends its
+  // range on the 2^kPScaleLog2 scale, so the fp8 path keeps the exact maximum.
+  static constexpr float kLazyLimit = 256.f;  // 2^8: largest p the bf16 path allows
+  static_assert(kLoadsPerWave >= 1 && kLoadsPerWave * kThreads * 16 == kTileBytes,
+                "K tile must split into whole lane loads");
+  static_assert(kVLoadsPerWave >= 1 && kVLoadsPerWave * kThreads * 16 == kVTileBytes,
+                "V tile must split into whole lane loads");
+  static_assert(!kFp8 || kBN == 64, "the fp8 P.V step consumes exactly one 64-key tile");
+
+  // identity
+  int lane, col, half, g, gi;
+  int wave_q0, qi;       // first query row of this wave / this lane's row (in doc)
+  // operands and state
+  bf16x8 qreg[kKSteps];
+  f32x16 oacc[kDBlocks];
+  f32x16 sacc[kKeyBlocks];
+  bf16x8 pb[kBN / 16];   // bf16 P of the last softmaxed tile
+  i32x8 pb8;             // e4m3 P of the last softmaxed tile
+  float m_run, l_run, c;
+  // per-lane LDS byte offsets of the operand reads within a stage's tile
+  int k_off[kKSteps];
+  int v_off[kVReads][kDBlocks];
+  // HBM -> LDS copy
+  i32x4 k_rsrc, v_rsrc;
+  uint32_t k_stride, v_stride;
+  int k_voff[kLoadsPerWave], v_voff[kVLoadsPerWave];
+
+  __device__ __forceinline__ void init(const FwdParams& p, const WorkItem& w, int wave,
+                                       int row_chunk) {
+    lane = threadIdx.x & 63;
+    col = lane & 31;
+    half = lane >> 5;
+    g = lane >> 4;
+    gi = lane & 15;
+    wave_q0 = w.m0 + 32 * row_chunk;
+    qi = wave_q0 + col;
+    c = p.scale_log2;
+    m_run = -__builtin_inff();
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+
+    // Q: the B operand of S^T = K Q^T, held in registers for the whole loop
+    {
+      const int row_stride = p.heads * kD;
+      const int qrow = w.q_start + min(qi, w.sq - 1);
+      const bf16_t* qp = (const bf16_t*)p.q + (size_t)qrow * row_stride + w.head * kD + 8 * half;
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t) qreg[t] = *(const bf16x8*)(qp + 16 * t);
+      // Q has landed before the K/V stream starts, so no wait on the stream's
+      // vector-memory counter is ever needed for Q inside the tile loop
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+
+    // operand read offsets. K rows 32*kb + col at logical chunk 2t + half.
+    // bf16 V (tr16): rows 16*ks16 + 8r + 4*half + gi/4, d = 32*db + 16*(g&1) + 4*(gi&3).
+    // fp8 V (tr8): rows 32*(r>>1) + 16*(r&1) + 8*(e>>2) + 4*half + (e&3), e = gi/2,
+    //              byte column 32*db + 16*(g&1) + 8*(gi&1).
+    // Key block, 16-key step and read index only add multiples of 16 rows,
+    // which the swizzle ignores, so they are immediates at the read sites.
+#pragma unroll
+    for (int t = 0; t < kKSteps; ++t)
+      k_off[t] = col * kRowBytes + (((2 * t + half) ^ swz<kChunks>(col)) * 16);
+#pragma unroll
+    for (int r = 0; r < kVReads; ++r)
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db) {
+        if constexpr (!kFp8) {
+          const int row = 8 * r + 4 * half + gi / 4;
+          const int d = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
+          v_off[r][db] = row * kVRowBytes + (((d / 8) ^ swz<kVChunks>(row)) * 16) + (d % 8) * 2;
+        } else {
+          const int e = gi >> 1;
+          const int row = 8 * (e >> 2) + 4 * half + (e & 3);
+          const int byte_col = 32 * db + 16 * (g & 1) + 8 * (gi & 1);
+          v_off[r][db] =
+              row * kVRowBytes + (((byte_col / 16) ^ swz<kVChunks>(row)) * 16) + (byte_col % 16);
+        }
+      }
+
+    // HBM -> LDS copy. Each wave copies 1 KB blocks: lane l lands at byte 16*l
+    // of the block, so the swizzle is applied by choosing which global chunk
+    // each lane fetches. Offsets are relative to this (document, head); rows
+    // past the document end fall outside the buffer and arrive as zeros.
+    k_stride = (uint32_t)p.heads * kRowBytes;
+    v_stride = (uint32_t)p.heads * kVRowBytes;
+    k_rsrc = make_buffer_rsrc((const char*)p.k + (size_t)w.k_start * k_stride + w.head * kRowBytes,
+                              (uint32_t)w.sk * k_stride);
+    v_rsrc = make_buffer_rsrc((const char*)p.v + (size_t)w.k_start * v_stride + w.head * kVRowBytes,
+                              (uint32_t)w.sk * v_stride);
+#pragma unroll
+    for (int r = 0; r < kLoadsPerWave; ++r) {
+      const int byte = 1024 * (r * kWaves + wave) + 16 * lane;
+      const int row = byte / kRowBytes;
+      const int phys = (byte % kRowBytes) / 16;
+      k_voff[r] = row * (int)k_stride + (phys ^ swz<kChunks>(row)) * 16;
+    }
+#pragma unroll
+    for (int r = 0; r < kVLoadsPerWave; ++r) {
+      const int byte = 1024 * (r * kWaves + wave) + 16 * lane;
+      const int row = byte / kVRowBytes;
+      const int phys = (byte % kVRowBytes) / 16;
+      v_voff[r] = row * (int)v_stride + (phys ^ swz<kVChunks>(row)) * 16;
+    }
+  }
+
+  // This wave's share of the copy of K tile j into K stage kStage (lds_k0 is
+  // the LDS address of this wave's first 1 KB block in stage 0): instruction r
+  // of kLoadsPerWave, or all of them. V likewise.
+  template <int kStage, int kR>
+  __device__ __forceinline__ void copy_k_one(int j, uint32_t lds_k0) {
+    lds_dma_16<kStage * kTileBytes + 1024 * kWaves * kR>(
+        lds_k0, k_voff[kR], k_rsrc, (int)((uint32_t)(j * kBN) * k_stride));
+  }
+  template <int kStage, int kR>
+  __device__ __forceinline__ void copy_v_one(int j, uint32_t lds_v0) {
+    lds_dma_16<kStage * kVTileBytes + 1024 * kWaves * kR>(
+        lds_v0, v_voff[kR], v_rsrc, (int)((uint32_t)(j * kBN) * v_stride));
+  }
+  template <int kStage>
+  __device__ __forceinline__ void copy_k(int j, uint32_t lds_k0) {
+    [&]<int... kR>(std::integer_sequence<int, kR...>) {
+      (copy_k_one<kStage, kR>(j, lds_k0), ...);
+    }(std::make_integer_sequence<int, kLoadsPerWave>());
+  }
+  template <int kStage>
+  __device__ __forceinline__ void copy_v(int j, uint32_t lds_v0) {
+    [&]<int... kR>(std::integer_sequence<int, kR...>) {
+      (copy_v_one<kStage, kR>(j, lds_v0), ...);
+    }(std::make_integer_sequence<int, kVLoadsPerWave>());
+  }
+
+  // Does any of this wave's rows see a key of tile j?
+  __device__ __forceinline__ bool active(int j, int causal_off) const {
+    return !kCausal || (j * kBN <= wave_q0 + 31 + causal_off);
+  }
+
+  // S^T = K Q^T for the 64 keys of the tile at ks (LDS, generic pointer).
+  __device__ __forceinline__ void qk(const char* ks) {
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+    // K operands are read kPrefetch steps ahead of their MFMAs (a ring of
+    // kPrefetch + 1 register sets), so the LDS latency hides behind the MFMAs
+    // of the steps in between. The scheduling-group barriers keep the compiler
+    // from pulling the reads back next to their uses.
+    constexpr int kPrefetch = 2;
+    bf16x8 ka[kPrefetch + 1][kKeyBlocks];
+#pragma unroll
+    for (int t = 0; t < kPrefetch && t < kKSteps; ++t)
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+        ka[t][kb] = *(const bf16x8*)(ks + k_off[t] + kb * 32 * kRowBytes);
+#pragma unroll
+    for (int t = 0; t < kKSteps; ++t) {
+      if (t + kPrefetch < kKSteps) {
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+          ka[(t + kPrefetch) % (kPrefetch + 1)][kb] =
+              *(const bf16x8*)(ks + k_off[t + kPrefetch] + kb * 32 * kRowBytes);
+      }
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kPrefetch + 1)][kb], qreg[t],
+                                                            sacc[kb], 0, 0, 0);
+    }
+    // schedule: the first kPrefetch steps' reads, then per step its reads
+    // for step t + kPrefetch followed by its MFMAs
+    constexpr int kFirstReads = (kPrefetch < kKSteps ? kPrefetch : kKSteps) * kKeyBlocks;
+    __builtin_amdgcn_sched_group_barrier(0x100, kFirstReads, 0);
+#pragma unroll
+    for (int t = 0; t < kKSteps; ++t) {
+      if (t + kPrefetch < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, kKeyBlocks, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kKeyBlocks, 0);
+    }
+  }
+
+  // Causal mask (key j visible to query i iff j <= i + sk - sq) and key tail
+  // (j < sk), on tiles that need it; then the online softmax and P.
+  __device__ __forceinline__ void softmax(int j, int sk, int causal_off) {
+    const int kt0 = j * kBN;
+    const bool need_mask = (kt0 + kBN > sk) || (kCausal && (kt0 + kBN - 1 > wave_q0 + causal_off));
+    if (need_mask) {
+      const int lim = kCausal ? min(sk - 1, qi + causal_off) : sk - 1;
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt0 + 32 * kb + (i / 4) * 8 + 4 * half + (i % 4);
+          if (key > lim) sacc[kb][i] = -__builtin_inff();
+        }
+    }
+    if constexpr (!kFp8) {
+      softmax_lazy();
+    } else {
+      softmax_exact();
+    }
+  }
+
+  // bf16 P: lazy maximum. The maximum in use (m_run) is kept as long as every
+  // p = exp2(c*s - c*m_run) of the tile stays <= 2^kLazyLog2, which is checked
+  // after the fact on each lane's partial row sum (every p is at most that
+  // sum). Only when some row of the wave exceeds it (or has no maximum yet)
+  // does the wave compute the tile's row maxima, rescale O and l, and redo p.
+  // The scores stay in sacc, so the redo needs no second Q.K^T. Rows whose
+  // maximum is not raised see alpha = 1 exactly, so each row's arithmetic
+  // depends on its own scores only. Any m gives the same O and LSE in exact
+  // arithmetic; m only bounds p.
+  __device__ __forceinline__ void softmax_lazy() {
+    float rs[4];
+    exp_sum_convert(rs);
+    float lane_sum = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    // NaN-safe: inf or NaN sums also take the slow path
+    const bool raise = (m_run == -__builtin_inff()) || !(lane_sum <= kLazyLimit);
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(raise);
+    if (mask != 0) {
+      // row n is raised if either of its lanes (n, n+32) asked for it
+      const uint32_t rows = (uint32_t)mask | (uint32_t)(mask >> 32);
+      const bool row_raise = (rows >> col) & 1u;
+      const float mx = tile_row_max();
+      // rows that see no key yet keep m_run = -inf (their p are all zero);
+      // rows not raised recompute bit-identical p
+      const bool up = row_raise && (mx > m_run);
+      const float alpha = up ? __builtin_amdgcn_exp2f((m_run - mx) * c) : 1.f;
+      m_run = up ? mx : m_run;
+      rescale(alpha);
+      exp_sum_convert(rs);
+      lane_sum = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
+    // l_run holds this lane's half of the keys; the halves are added at the end
+    l_run += lane_sum;
+  }
+
+  // e4m3 P: the exact running maximum, so that 2^kPScaleLog2 * p <= 2^8 fits
+  // e4m3's range (max 448) without saturation.
+  __device__ __forceinline__ void softmax_exact() {
+    const float mx = tile_row_max();
+    // NaN when both are -inf (a row with nothing visible yet): no raise
+    const bool raise = mx > m_run;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      // raise implies mx finite; alpha = 0 when m_run = -inf
+      const float alpha = raise ? __builtin_amdgcn_exp2f((m_run - mx) * c) : 1.f;
+      m_run = raise ? mx : m_run;
+      rescale(alpha);
+    }
+    float rs[4];
+    exp_sum_convert(rs);
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  }
+
+  // Row maximum of the tile's scores over both lane halves. Four independent
+  // partial maxima keep the dependency chains short.
+  __device__ __forceinline__ float tile_row_max() const {
+    float mp[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], sacc[kb][i]);
+    return wave_half_swap_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+  }
+
+  __device__ __forceinline__ void rescale(float alpha) {
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+  }
+
+  // p = exp2(fma(s, c, -c*m_run)) for the 32 scores of this lane (the scale and
+  // the row maximum folded into one multiply-add), partial row sums of the fp32
+  // p in four chains, and P rounded for the P.V operand (bf16 RNE, or e4m3 with
+  // 2^kPScaleLog2 folded into the exponent). The scores in sacc are kept.
+  __device__ __forceinline__ void exp_sum_convert(float (&rs)[4]) {
+    // an all-masked row keeps the fold finite
+    const float neg_mc = (m_run == -__builtin_inff()) ? 0.f : -m_run * c;
+    const float p_add = kFp8 ? neg_mc + kPScaleLog2 : neg_mc;
+    rs[0] = rs[1] = rs[2] = rs[3] = 0.f;
+    if constexpr (!kFp8) {
+      static_for<kBN / 16>([&](auto ks_tag) {
+        constexpr int ks16 = decltype(ks_tag)::value;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float pv = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sacc[ks16 / 2][8 * (ks16 % 2) + jj], c, p_add));
+          rs[jj & 3] += pv;
+          pb[ks16][jj] = (bf16_t)pv;
+        }
+      });
+    } else {
+      // Byte j of a lane's operand is key kappa(half, j) =
+      //   32*(j/16) + 8*((j%16)/4) + 4*half + j%4,
+      // which is where the S^T accumulator left P; V is fetched to match.
+      static_for<8>([&](auto w_tag) {
+        constexpr int w = decltype(w_tag)::value;
+        constexpr int kb = w / 4, i0 = 4 * (w % 4);
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + e], c, p_add));
+          rs[e] += pv[e];
+        }
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
+        pb8[w] = word;
+      });
+    }
+  }
+
+  // O^T += V^T P^T for the tile at vs (LDS, generic pointer).
+  __device__ __forceinline__ void pv(const char* vs) {
+    if constexpr (!kFp8) {
+      // 16 keys per MFMA. Lane (half, m) needs V[keys 16*ks16 + 8r + 4*half
+      // + 0..3][d = 32*db + m]; source lane gi of group g reads 4 d-values of
+      // key row (.. + gi/4). The A operands of MFMA i + kAhead are read while
+      // MFMA i runs (a ring of kAhead + 1 operand sets), which bounds the
+      // registers the reads in flight take.
+      constexpr int kN = (kBN / 16) * kDBlocks;   // MFMAs per tile
+      constexpr int kAhead = 3;
+      bf16x8 va[kAhead + 1];
+      auto read_v = [&](int i) {
+        const int ks16 = i / kDBlocks, db = i % kDBlocks;
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(vs + v_off[0][db] + 16 * ks16 * kVRowBytes));
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(vs + v_off[1][db] + 16 * ks16 * kVRowBytes));
+        va[i % (kAhead + 1)] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) read_v(i);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        if (i + kAhead < kN) read_v(i + kAhead);
+        const int ks16 = i / kDBlocks, db = i % kDBlocks;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % (kAhead + 1)], pb[ks16], oacc[db],
+                                                           0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      }
+    } else {
+      // all 64 keys of the tile in one e4m3 MFMA per d block
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db) {
+        i32x8 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // read r delivers bytes 8r..8r+7: keys 32*(r>>1) + 16*(r&1) + ...
+          const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (LDS_AS i32x2*)(vs + v_off[0][db] + (32 * (r >> 1) + 16 * (r & 1)) * kVRowBytes));
+          a[2 * r] = t[0];
+          a[2 * r + 1] = t[1];
+        }
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb8, oacc[db], 0, 0, 0, 127,
+                                                                   0, 127);
+      }
+    }
+  }
+
+  // O /= l -> bf16 store; LSE = scale*m + ln(l) (natural log). A row with no
+  // visible key has l = 0: O = 0 and LSE = -inf.
+  __device__ __forceinline__ void epilogue(const FwdParams& p, const WorkItem& w) {
+    l_run = wave_half_swap_sum(l_run);
+    if (qi >= w.sq) return;
+    // fp8: O = v_scale * sum(P_hat V_codes) / l, where l carries the same 2^kPScaleLog2
+    const float num_scale = kFp8 ? p.v_scale[w.head] : 1.f;
+    const float inv_l = (l_run > 0.f) ? num_scale / l_run : 0.f;
+    const int row_stride = p.heads * kD;
+    bf16_t* op = (bf16_t*)p.out + (size_t)(w.q_start + qi) * row_stride + w.head * kD;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int d0 = 32 * db + 8 * ig + 4 * half;
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (bf16_t)(oacc[db][4 * ig + e] * inv_l);
+        *(bf16x4*)(op + d0) = o4;
+      }
+    if (p.lse != nullptr && half == 0) {
+      float lse = -__builtin_inff();
+      const float lsub = kFp8 ? kPScaleLog2 : 0.f;
+      if (l_run > 0.f)
+        lse = (m_run * c + (__builtin_amdgcn_logf(l_run) - lsub)) * 0.69314718055994531f;
+      p.lse[(size_t)w.head * p.total_q + w.q_start + qi] = lse;
+    }
+  }
+};
+
+}  // namespace fmha
+
+#endif  // FMHA_DEVICE_H_

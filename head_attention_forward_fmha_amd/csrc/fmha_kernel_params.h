@@ -26,8 +26,15 @@ struct FwdParams {
   int32_t n_mblocks;      // query blocks per document (set by the launcher)
 };
 
-hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
-hipError_t launch_fwd_fp8pv(const FwdParams& p, int head_dim, bool causal, hipStream_t stream);
+// Kernel variants (the values of fmha.h's FMHA_VARIANT_*).
+constexpr int kVariantAuto = 0;      // pick by problem size
+constexpr int kVariantFourWave = 1;  // 4 waves, 128 query rows per workgroup
+constexpr int kVariantPingPong = 2;  // 8 waves in two phase-shifted groups, 256 rows
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, int variant,
+                           hipStream_t stream);
+hipError_t launch_fwd_fp8pv(const FwdParams& p, int head_dim, bool causal, int variant,
+                            hipStream_t stream);
 
 }  // namespace fmha
 

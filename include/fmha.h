@@ -108,6 +108,36 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
                              void* out, float* lse, void* stream);
 
 /*
+ * Kernel variant selection, for testing and tuning. FMHA_VARIANT_AUTO (what
+ * fmha_fwd and fmha_fwd_fp8pv use) takes the 8-wave ping-pong kernel when the
+ * problem has at least 512 blocks of 256 query rows, else the 4-wave kernel.
+ * All variants compute the same function; results may differ in the last bits
+ * of rounding (different tiling of the row-sum and the lazy maximum).
+ */
+#define FMHA_VARIANT_AUTO 0
+#define FMHA_VARIANT_FOUR_WAVE 1   /* 4 waves, 128 query rows per workgroup   */
+#define FMHA_VARIANT_PINGPONG 2    /* 8 waves in two phase-shifted groups     */
+
+/* fmha_fwd with an explicit kernel variant (any other value: INVALID_ARG). */
+fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads, int32_t head_dim,
+                               int32_t causal, float softmax_scale,
+                               void* out, float* lse, int32_t variant, void* stream);
+
+/* fmha_fwd_fp8pv with an explicit kernel variant (any other value: INVALID_ARG). */
+fmha_status_t fmha_fwd_fp8pv_variant(const void* q, const void* k, const uint8_t* v_e4m3,
+                                     const float* v_scale,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t total_q, int32_t total_k,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_heads, int32_t head_dim,
+                                     int32_t causal, float softmax_scale,
+                                     void* out, float* lse, int32_t variant, void* stream);
+
+/*
  * Host-side check of a cu_seqlens array (HOST pointer, batch + 1 entries):
  * starts at 0, is non-decreasing, ends at total, and no document is longer
  * than max_seqlen. Returns FMHA_OK or FMHA_ERR_INVALID_ARG. Makes no HIP call.

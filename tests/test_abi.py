@@ -23,7 +23,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == sorted(["fmha_fwd", "fmha_fwd_fp8pv", "fmha_validate_cu_seqlens",
+    assert names == sorted(["fmha_fwd", "fmha_fwd_fp8pv", "fmha_fwd_variant",
+                            "fmha_fwd_fp8pv_variant", "fmha_validate_cu_seqlens",
                             "fmha_status_string", "fmha_abi_version"])
 
 
@@ -80,6 +81,18 @@ def test_fwd_rejects_bad_arguments(kw, status):
     assert _call_fwd(**kw) == status
 
 
+def test_variant_must_be_known():
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    args = [0x10000, 0x20000, 0x30000, None, None, 1, 128, 128, 128, 128, 2, 64, 0,
+            ctypes.c_float(0.125), 0x40000, 0x50000]
+    assert lib.fmha_fwd_variant(*args, 3, None) == 1
+    assert lib.fmha_fwd_variant(*args, -1, None) == 1
+    fargs = [0x10000, 0x20000, 0x30000, 0x70000, None, None, 1, 128, 128, 128, 128, 2, 128, 0,
+             ctypes.c_float(0.125), 0x40000, 0x50000]
+    assert lib.fmha_fwd_fp8pv_variant(*fargs, 7, None) == 1
+
+
 def test_fwd_empty_problem_is_a_no_op():
     # no kernel is launched (so no GPU is needed) when there is nothing to compute
     assert _call_fwd(batch=0, total_q=0, total_k=0, max_q=0, max_k=0, q=None, k=None, v=None,
@@ -113,14 +126,24 @@ def test_validate_cu_seqlens(cu, total, max_s, ok):
 
 def test_resource_gate_parser():
     from head_attention_forward_fmha_amd.build import check_resources, parse_resource_report
-    text = ("remark: a.hip:1:0: Function Name: kern [-Rpass-analysis=kernel-resource-usage]\n"
-            "remark: a.hip:1:0:     VGPRs: 200 [-Rpass-analysis=kernel-resource-usage]\n"
-            "remark: a.hip:1:0:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]\n"
-            "remark: a.hip:1:0:     VGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]\n")
+    # the format clang prints: location first, then "remark:"
+    r = "[-Rpass-analysis=kernel-resource-usage]"
+    text = (f"a.hip:10:1: remark: Function Name: kern {r}\n"
+            "   10 | void kern() {\n"
+            f"a.hip:10:1: remark:     VGPRs: 200 {r}\n"
+            f"a.hip:10:1: remark:     ScratchSize [bytes/lane]: 16 {r}\n"
+            f"a.hip:10:1: remark:     SGPRs Spill: 0 {r}\n"
+            f"a.hip:10:1: remark:     VGPRs Spill: 3 {r}\n"
+            f"a.hip:20:1: remark: Function Name: good {r}\n"
+            f"a.hip:20:1: remark:     ScratchSize [bytes/lane]: 0 {r}\n"
+            f"a.hip:20:1: remark:     SGPRs Spill: 0 {r}\n"
+            f"a.hip:20:1: remark:     VGPRs Spill: 0 {r}\n")
     k = parse_resource_report(text)
-    assert k["kern"]["VGPRs"] == "200"
+    assert k["kern"]["VGPRs"] == "200" and k["kern"]["VGPRs Spill"] == "3"
     bad = check_resources(k)
-    assert len(bad) == 2
+    assert len(bad) == 2 and all(b.startswith("kern") for b in bad)
+    # a kernel whose report lacks the fields fails too
+    assert check_resources({"x": {}})
 
 
 def test_built_kernels_have_no_scratch_or_spills():
@@ -129,5 +152,5 @@ def test_built_kernels_have_no_scratch_or_spills():
     if not os.path.exists(RESOURCE_REPORT):
         pytest.skip("resource report not present (library built elsewhere)")
     kernels = parse_resource_report(open(RESOURCE_REPORT).read())
-    assert any("fmha_fwd_kernel" in k for k in kernels)
+    assert sum("fmha_fwd" in k for k in kernels) >= 12
     assert check_resources(kernels) == []

@@ -23,6 +23,8 @@ from synthetic import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
+VARIANTS = ["four_wave", "pingpong"]
+
 O_ATOL = O_RTOL = 1e-2
 O_ATOL_FP8 = O_RTOL_FP8 = 5e-2
 LSE_ATOL = 1e-3
@@ -34,7 +36,7 @@ def _dev():
     return torch.device("cuda:0")
 
 
-def _run(inp, causal, scale, heads, d, fp8=False, max_q=None, max_k=None):
+def _run(inp, causal, scale, heads, d, fp8=False, max_q=None, max_k=None, variant="auto"):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     q, k = inp.q.to(dev), inp.k.to(dev)
@@ -48,10 +50,10 @@ def _run(inp, causal, scale, heads, d, fp8=False, max_q=None, max_k=None):
     lse = torch.full((heads, q.shape[0]), float("nan"), dtype=torch.float32, device=dev)
     if fp8:
         fm.fwd_fp8pv(q, k, inp.v_e4m3.to(dev), inp.v_scale.to(dev), cq, ck, mq, mk, causal=causal,
-                     softmax_scale=scale, out=out, lse=lse)
+                     softmax_scale=scale, out=out, lse=lse, variant=variant)
     else:
         fm.fwd(q, k, inp.v.to(dev), cq, ck, mq, mk, causal=causal, softmax_scale=scale, out=out,
-               lse=lse)
+               lse=lse, variant=variant)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -72,16 +74,18 @@ def _check(o, lse, o_ref, lse_ref, fp8=False, what=""):
         assert lerr.max() <= LSE_ATOL, f"{what}: LSE max err {lerr.max():.3e}"
 
 
-def _full_parity(lens, heads, d, causal, seed=0, scale=None, fp8=False, max_q=None, max_k=None):
+def _full_parity(lens, heads, d, causal, seed=0, scale=None, fp8=False, max_q=None, max_k=None,
+                 variant="auto"):
     inp = make_inputs(lens, heads, d, seed=seed, fp8_pv=fp8)
     scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
-    o, lse = _run(inp, causal, scale, heads, d, fp8=fp8, max_q=max_q, max_k=max_k)
+    o, lse = _run(inp, causal, scale, heads, d, fp8=fp8, max_q=max_q, max_k=max_k, variant=variant)
     if fp8:
         o_ref, lse_ref = oracle.attention_fp8pv(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
                                                 inp.cu_k, causal, scale)
     else:
         o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
-    _check(o, lse, o_ref, lse_ref, fp8=fp8, what=f"lens={lens} h={heads} d={d} causal={causal}")
+    _check(o, lse, o_ref, lse_ref, fp8=fp8,
+           what=f"lens={lens} h={heads} d={d} causal={causal} variant={variant}")
     return inp, o, lse
 
 
@@ -169,8 +173,9 @@ def test_c5_causal_fp8pv_32k_sampled():
 ])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-def test_ragged_lengths(lens, causal, d):
-    _full_parity(lens, 3, d, causal, seed=len(lens) + d)
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_ragged_lengths(lens, causal, d, variant):
+    _full_parity(lens, 3, d, causal, seed=len(lens) + d, variant=variant)
 
 
 @pytest.mark.parametrize("lens", [
@@ -178,32 +183,50 @@ def test_ragged_lengths(lens, causal, d):
     ((5, 5), (0, 0), (130, 7), (7, 130)),
 ])
 @pytest.mark.parametrize("causal", [False, True])
-def test_unequal_and_empty_documents(lens, causal):
-    _full_parity(lens, 2, 128, causal, seed=7)
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_unequal_and_empty_documents(lens, causal, variant):
+    _full_parity(lens, 2, 128, causal, seed=7, variant=variant)
 
 
-def test_many_small_documents():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_many_small_documents(variant):
     rng = np.random.default_rng(3)
     lens = tuple((int(x), int(x)) for x in rng.integers(0, 200, 40))
     for causal in (False, True):
-        _full_parity(lens, 4, 128, causal, seed=11)
+        _full_parity(lens, 4, 128, causal, seed=11, variant=variant)
 
 
-def test_fp8_small_cases():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_fp8_small_cases(variant):
     for lens, causal in ((((200, 200),), True), (((129, 129), (64, 64)), False),
-                         (((100, 300), (300, 100)), True)):
-        _full_parity(lens, 2, 128, causal, fp8=True, seed=13)
+                         (((100, 300), (300, 100)), True), (((600, 600), (1, 1)), True)):
+        _full_parity(lens, 2, 128, causal, fp8=True, seed=13, variant=variant)
 
 
-def test_nonstandard_scale_and_large_scores():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_nonstandard_scale_and_large_scores(variant):
     # a large scale makes every row nearly one-hot: the max-subtraction must hold
-    _full_parity(((256, 256),), 2, 128, True, scale=1.0, seed=17)
-    _full_parity(((256, 256),), 2, 64, False, scale=0.5, seed=18)
+    _full_parity(((256, 256),), 2, 128, True, scale=1.0, seed=17, variant=variant)
+    _full_parity(((600, 600),), 2, 64, False, scale=0.5, seed=18, variant=variant)
 
 
-def test_max_seqlen_larger_than_needed():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_max_seqlen_larger_than_needed(variant):
     # a generous max_seqlen only adds empty work items
-    _full_parity(((100, 100), (50, 50)), 2, 128, True, max_q=1000, max_k=1000, seed=19)
+    _full_parity(((100, 100), (50, 50)), 2, 128, True, max_q=1000, max_k=1000, seed=19,
+                 variant=variant)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_kernel_variants_agree_bitwise(causal, fp8):
+    """Both kernels run the same per-row arithmetic in the same tile order."""
+    lens = ((1000, 1000), (333, 333), (1, 1), (700, 701))
+    inp = make_inputs(lens, 4, 128, seed=29, fp8_pv=fp8)
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    o1, l1 = _run(inp, causal, scale, 4, 128, fp8=fp8, variant="four_wave")
+    o2, l2 = _run(inp, causal, scale, 4, 128, fp8=fp8, variant="pingpong")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 # ---------------------------------------------------------------- bitwise properties
