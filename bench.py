@@ -12,16 +12,18 @@ steps; GPU events on the stream the kernel runs on). value = counted FLOP of
 K steps / elapsed time, with FLOP = 4*h*sum(sq*sk)*d halved for causal.
 
 Extra objects on the same line:
-  roofline      achieved TFLOP/s of the FMHA kernel against MI355X's published
-                dense bf16 MFMA peak, plus HBM traffic from committed rocprofv3
-                counter summaries when they were taken on the current kernel
-                source (else null);
+  roofline      counted FLOP per launch / average launch duration (per-step
+                events) against MI355X's published dense bf16 MFMA peak, plus
+                HBM traffic per launch from committed rocprofv3 counter
+                summaries when they were taken on the current kernel sources
+                (else null);
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
-                the same workload (one document, several heads), in the same unit.
+                the same workload (whole document x head units), in the same unit.
 
 Options: --workload c1|c2|c3|c4|c5 (other workloads, for measurement only),
---no-cpu-baseline, --counters (a short run for rocprofv3 --pmc: a copy kernel
-of known size, then a few steps).
+--variant, --no-cpu-baseline, --counters (a short run for rocprofv3 --pmc: a
+copy kernel of known size, then a few steps), --summarize-counters and
+--summarize-trace (turn rocprofv3 CSV output into the committed summaries).
 """
 
 from __future__ import annotations
@@ -38,16 +40,29 @@ sys.path.insert(0, ROOT)
 
 MI355X_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # published dense MFMA peaks
 MI355X_HBM_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "head_attention_forward_fmha_amd", "csrc", "fmha_fwd_kernel.hip")
+CSRC = os.path.join(ROOT, "head_attention_forward_fmha_amd", "csrc")
+KERNEL_SOURCES = ("fmha_fwd_kernel.hip", "fmha_device.h", "fmha_kernel_params.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fmha_fwd_traffic.json")
+KERNEL_NAMES = {"four_wave": "fmha::fmha_fwd_kernel", "pingpong": "fmha::fmha_fwd_pingpong_kernel"}
+# counted FLOP of the oracle sample: about 10-30 s of fp64 numpy on a 16-core host
+CPU_SAMPLE_FLOP = 4e11
 
 SHORT = {"c1": "c1_tiny_dense", "c2": "c2_dense_2225", "c3": "c3_varlen_causal_8k",
          "c4": "c4_varlen_causal_32k", "c5": "c5_causal_fp8pv_32k"}
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the device sources; counter figures taken on other sources are stale."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_template_name(w, variant):
+    return (f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}, "
+            f"{str(w.fp8_pv).lower()}>")
 
 
 def parse_args():
@@ -59,9 +74,15 @@ def parse_args():
     ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong"],
                     help="kernel variant (auto picks by problem size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-heads", type=int, default=16)
+    ap.add_argument("--cpu-sample-flop", type=float, default=CPU_SAMPLE_FLOP,
+                    help="counted FLOP of the oracle sample (whole document x head units)")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: copy kernel of known size, then steps")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --counters run into an entry of the traffic file")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="print a rocprofv3 --stats kernel_stats.csv as a text table")
     return ap.parse_args()
 
 
@@ -122,47 +143,52 @@ def time_steps(step, steps, warmup):
     return total_ms, each
 
 
-def load_traffic(w):
-    """Per-launch HBM bytes from committed counter summaries, if current."""
+def load_traffic(w, variant):
+    """Per-launch HBM bytes from committed counter summaries, if taken on these sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        entry = t.get(w.name)
-        if entry is None or entry.get("kernel_source_sha256_16") != kernel_source_hash():
-            return None
-        return float(entry["hbm_bytes_per_launch"])
-    except Exception:
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    entry = t.get(f"{w.name}/{variant}")
+    if entry is None or entry.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
+    return float(entry["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, inp, sample_heads):
-    """Time the fp64 oracle on one document x sample_heads heads of the workload."""
+def cpu_baseline(w, inp, sample_flop):
+    """Time the fp64 oracle on a bounded sample of the workload.
+
+    The sample is whole (document, head) units, longest documents first and heads
+    in order, until their counted FLOP (the same convention as the GPU figure)
+    reaches sample_flop or the workload is exhausted."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    cu_q = np.asarray(inp.cu_q)
-    doc = int(np.argmax(np.diff(cu_q)))
-    heads = list(range(min(sample_heads, w.heads)))
-    sq = int(cu_q[doc + 1] - cu_q[doc])
-    v = inp.v
-    if w.fp8_pv:
-        v = oracle.dequantize_v(inp.v_e4m3, inp.v_scale)
-    t0 = time.perf_counter()
-    oracle.attention(inp.q, inp.k, v, inp.cu_q, inp.cu_k, w.causal, w.softmax_scale,
-                     heads=heads, docs=[doc])
-    dt = time.perf_counter() - t0
-    flops = 4.0 * len(heads) * sq * sq * w.head_dim / (2.0 if w.causal else 1.0)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    cu_q, cu_k = np.asarray(inp.cu_q), np.asarray(inp.cu_k)
+    order = sorted(range(len(cu_q) - 1), key=lambda b: -(cu_q[b + 1] - cu_q[b]))
+    v = oracle.dequantize_v(inp.v_e4m3, inp.v_scale) if w.fp8_pv else inp.v
+    done, units, parts, dt = 0.0, 0, [], 0.0
+    for b in order:
+        sq, sk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
+        per_head = 4.0 * sq * sk * w.head_dim / (2.0 if w.causal else 1.0)
+        if per_head == 0:
+            continue
+        n_heads = int(min(w.heads, max(1, np.ceil((sample_flop - done) / per_head))))
+        t0 = time.perf_counter()
+        oracle.attention(inp.q, inp.k, v, inp.cu_q, inp.cu_k, w.causal, w.softmax_scale,
+                         heads=list(range(n_heads)), docs=[b])
+        dt += time.perf_counter() - t0
+        done += n_heads * per_head
+        units += n_heads
+        parts.append(f"doc {b} ({sq} tokens) x {n_heads} heads")
+        if done >= sample_flop:
+            break
+    return {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"document {doc} ({sq} tokens) x {len(heads)} of {w.heads} heads, "
-                      f"fp64 numpy, {dt:.1f} s wall; same FLOP count convention"}
+            "sample": f"{units} (document, head) units: {'; '.join(parts)}; "
+                      f"{done / 1e9:.1f} GFLOP counted, fp64 numpy, {dt:.1f} s wall"}
 
 
 def run_counters(w, d, step):
@@ -180,8 +206,83 @@ def run_counters(w, d, step):
     print(json.dumps({"counters_run": w.name, "copy_bytes": n, "steps": 3}), flush=True)
 
 
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_csv, write_csv, copy_bytes=256 * 1024 * 1024):
+    """HBM bytes per FMHA launch from a --counters run under rocprofv3 --pmc.
+
+    FETCH_SIZE and WRITE_SIZE are KiB per dispatch. Each is scaled by the ratio of
+    the bytes the copy kernel of known size moved to what the counter read for it,
+    then averaged over the FMHA dispatches of the run."""
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:
+            key = (r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        copies = [v for (_, name, grid), v in per.items()
+                  if "copyBuffer" in name and v * 1024 > copy_bytes / 8]
+        fmha = [(name, v) for (_, name, _), v in per.items() if "fmha_fwd" in name]
+        if len(copies) != 1 or not fmha:
+            raise SystemExit(f"{path}: expected one {copy_bytes}-byte copy and FMHA dispatches")
+        factor = copy_bytes / (copies[0] * 1024)
+        names = {n for n, _ in fmha}
+        if len(names) != 1:
+            raise SystemExit(f"{path}: more than one FMHA kernel: {sorted(names)}")
+        kib = sum(v for _, v in fmha) / len(fmha)
+        out[counter] = {"kib_per_dispatch": kib, "copy_factor": factor,
+                        "bytes_per_launch": kib * 1024 * factor, "dispatches": len(fmha),
+                        "kernel": names.pop()}
+    return out
+
+
+def summarize_trace(stats_csv):
+    rows = _counter_rows(stats_csv)
+    lines = [f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['Percentage']):>6.2f}  {r['Name']}")
+    return "\n".join(lines)
+
+
 def main():
     args = parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_counters:
+        # the counters must have been taken on the current sources: the entry is
+        # stamped with their hash, and a later change of the kernel voids it
+        from synthetic import WORKLOADS
+        w = WORKLOADS[SHORT.get(args.workload, args.workload)]
+        c = summarize_counters(*args.summarize_counters)
+        kernel = c["FETCH_SIZE"]["kernel"]
+        variant = "pingpong" if "pingpong" in kernel else "four_wave"
+        table = {}
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                table = json.load(f)
+        table[f"{w.name}/{variant}"] = {
+            "kernel": kernel, "kernel_source_sha256_16": kernel_source_hash(),
+            "hbm_bytes_per_launch": round(c["FETCH_SIZE"]["bytes_per_launch"] +
+                                          c["WRITE_SIZE"]["bytes_per_launch"]),
+            "algorithmic_hbm_bytes_per_launch": w.hbm_bytes(),
+            "fetch_kib_per_dispatch": round(c["FETCH_SIZE"]["kib_per_dispatch"], 1),
+            "fetch_copy_factor": round(c["FETCH_SIZE"]["copy_factor"], 4),
+            "write_kib_per_dispatch": round(c["WRITE_SIZE"]["kib_per_dispatch"], 1),
+            "write_copy_factor": round(c["WRITE_SIZE"]["copy_factor"], 4),
+            "dispatches": c["FETCH_SIZE"]["dispatches"]}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(table, f, indent=1, sort_keys=True)
+            f.write("\n")
+        print(json.dumps(table[f"{w.name}/{variant}"], indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this FMHA forward pass has no multi-GPU path "
               "(heads/documents would shard across GPUs with no exchange); run with --gpus 1",
@@ -189,6 +290,7 @@ def main():
         sys.exit(2)
     import torch
     from synthetic import WORKLOADS
+    import head_attention_forward_fmha_amd as fm
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(1)
@@ -204,19 +306,24 @@ def main():
     flops = w.flops()
     ms_per_step = total_ms / args.steps
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    # one launch per step: the per-step events bracket exactly one kernel
+    launch_ms = sum(each) / len(each)
+    achieved = flops / (launch_ms * 1e-3) / 1e12
     dtype = "bf16+fp8" if w.fp8_pv else "bf16"
     peak = MI355X_PEAK_TFLOPS["bf16"]
-    traffic = load_traffic(w)
-    roof = {"bound": "mfma", "achieved": round(value, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(value / peak, 4), "traffic": traffic,
-            "kernel": "fmha::fmha_fwd_kernel", "algorithmic_flop_per_launch": flops,
+    variant = (args.variant if args.variant != "auto"
+               else fm.auto_variant(w.batch, w.max_seqlen_q, w.heads))
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(w, variant),
+            "kernel": kernel_template_name(w, variant), "launch_avg_us": round(launch_ms * 1e3, 2),
+            "algorithmic_flop_per_launch": flops,
             "algorithmic_hbm_bytes_per_launch": w.hbm_bytes(),
-            "achieved_hbm_gbps": round(w.hbm_bytes() / (ms_per_step * 1e-3) / 1e9, 1)}
+            "algorithmic_hbm_gbps": round(w.hbm_bytes() / (launch_ms * 1e-3) / 1e9, 1)}
     if w.fp8_pv:
         # Q.K^T at the bf16 rate, P.V at the fp8 rate: the harmonic blend of the two peaks
         roof["peak_blended_bf16_fp8"] = 1.0 / (0.5 / MI355X_PEAK_TFLOPS["bf16"] +
                                                0.5 / MI355X_PEAK_TFLOPS["fp8"])
-        roof["frac_blended"] = round(value / roof["peak_blended_bf16_fp8"], 4)
+        roof["frac_blended"] = round(achieved / roof["peak_blended_bf16_fp8"], 4)
     line = {
         "metric": "FMHA fwd TFLOP/s and % of MI355X dense bf16 MFMA peak, d=128, 1 GPU",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -227,12 +334,12 @@ def main():
         "config": {"workload": w.description, "name": w.name, "total_tokens": w.total_q,
                    "docs": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "causal": w.causal, "seed": w.seed, "fp8_pv": w.fp8_pv,
-                   "kernel_variant": args.variant},
+                   "kernel_variant": variant},
         "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_heads)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_flop)
     print(json.dumps(line), flush=True)
 
 

@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import FMHA_OK, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8pv", "validate_cu_seqlens", "status_string", "abi_version",
+__all__ = ["fwd", "fwd_fp8pv", "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
            "FmhaError", "EXPORTED_SYMBOLS", "VARIANTS", "load_library"]
 
 
@@ -156,6 +156,14 @@ def fwd_fp8pv(q, k, v_e4m3, v_scale, cu_seqlens_q=None, cu_seqlens_k=None,
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_fwd_fp8pv")
     return out, lse
+
+
+def auto_variant(batch: int, max_seqlen_q: int, num_heads: int) -> str:
+    """Name of the kernel variant that variant="auto" runs for this problem size."""
+    v = load_library().fmha_fwd_auto_variant(int(batch), int(max_seqlen_q), int(num_heads))
+    if v < 0:
+        raise ValueError("negative problem size")
+    return {k: n for n, k in VARIANTS.items()}[v]
 
 
 def validate_cu_seqlens(cu_host, total: int, max_seqlen: int) -> bool:

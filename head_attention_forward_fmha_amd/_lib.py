@@ -25,6 +25,7 @@ EXPORTED_SYMBOLS = (
     "fmha_fwd_fp8pv",
     "fmha_fwd_variant",
     "fmha_fwd_fp8pv_variant",
+    "fmha_fwd_auto_variant",
     "fmha_validate_cu_seqlens",
     "fmha_status_string",
     "fmha_abi_version",
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmha_fwd_variant.restype = ctypes.c_int
     lib.fmha_fwd_fp8pv_variant.argtypes = _FWD_FP8_ARGS[:-1] + [_i32, _vp]
     lib.fmha_fwd_fp8pv_variant.restype = ctypes.c_int
+    lib.fmha_fwd_auto_variant.argtypes = [_i32, _i32, _i32]
+    lib.fmha_fwd_auto_variant.restype = ctypes.c_int32
     lib.fmha_validate_cu_seqlens.argtypes = [_vp, _i32, _i32, _i32]
     lib.fmha_validate_cu_seqlens.restype = ctypes.c_int
     lib.fmha_status_string.argtypes = [ctypes.c_int]

@@ -145,6 +145,11 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
                                 stream);
 }
 
+int32_t fmha_fwd_auto_variant(int32_t batch, int32_t max_seqlen_q, int32_t num_heads) {
+  if (batch < 0 || max_seqlen_q < 0 || num_heads < 0) return -1;
+  return fmha::resolve_variant(fmha::kVariantAuto, batch, max_seqlen_q, num_heads);
+}
+
 fmha_status_t fmha_validate_cu_seqlens(const int32_t* host_cu, int32_t batch, int32_t total,
                                        int32_t max_seqlen) {
   if (batch < 0 || total < 0 || max_seqlen < 0) return FMHA_ERR_INVALID_ARG;

@@ -31,6 +31,7 @@ namespace fmha {
 
 constexpr int kWaves4 = 4;
 constexpr int kBM4 = kWaves4 * 32;  // query rows per workgroup
+static_assert(kBM4 == kRowsFourWave, "4-wave block height");
 
 template <int kD, bool kCausal, bool kFp8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves4 * 64, kWaves4 * 64),
@@ -93,6 +94,7 @@ void fmha_fwd_kernel(FwdParams p) {
 
 constexpr int kWaves8 = 8;
 constexpr int kBM8 = kWaves8 * 32;  // query rows per workgroup
+static_assert(kBM8 == kRowsPingPong, "8-wave block height");
 constexpr int kStages8 = 3;         // K/V ring depth
 
 // Phase-boundary hooks for a coarse in-kernel timeline (s_memtime stamps). The
@@ -215,9 +217,7 @@ void fmha_fwd_pingpong_kernel(FwdParams p) {
 template <int kD, bool kCausal, bool kFp8>
 static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   FwdParams q = p;
-  const long long items8 = ((long long)p.max_seqlen_q + kBM8 - 1) / kBM8 * p.heads * p.batch;
-  // the 8-wave kernel needs enough 256-row blocks to fill the 256 CUs twice
-  const bool use8 = (variant == kVariantPingPong) || (variant == kVariantAuto && items8 >= 512);
+  const bool use8 = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads) == kVariantPingPong;
   const int bm = use8 ? kBM8 : kBM4;
   q.n_mblocks = (p.max_seqlen_q + bm - 1) / bm;
   const long long n_items = (long long)q.n_mblocks * p.heads * p.batch;

@@ -31,6 +31,20 @@ constexpr int kVariantAuto = 0;      // pick by problem size
 constexpr int kVariantFourWave = 1;  // 4 waves, 128 query rows per workgroup
 constexpr int kVariantPingPong = 2;  // 8 waves in two phase-shifted groups, 256 rows
 
+// Query rows per workgroup of each kernel.
+constexpr int kRowsFourWave = 128;
+constexpr int kRowsPingPong = 256;
+
+// The kernel a launch runs. Automatic selection takes the 8-wave kernel once the
+// problem has at least 512 blocks of 256 query rows (two per CU), else the
+// 4-wave kernel, whose smaller blocks fill the chip better on small problems.
+inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int32_t heads) {
+  if (variant != kVariantAuto) return variant;
+  const long long blocks = ((long long)max_seqlen_q + kRowsPingPong - 1) / kRowsPingPong *
+                           heads * batch;
+  return blocks >= 512 ? kVariantPingPong : kVariantFourWave;
+}
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, int variant,
                            hipStream_t stream);
 hipError_t launch_fwd_fp8pv(const FwdParams& p, int head_dim, bool causal, int variant,

@@ -138,6 +138,14 @@ fmha_status_t fmha_fwd_fp8pv_variant(const void* q, const void* k, const uint8_t
                                      void* out, float* lse, int32_t variant, void* stream);
 
 /*
+ * The kernel variant FMHA_VARIANT_AUTO resolves to for a problem of `batch`
+ * documents, longest query document max_seqlen_q and num_heads heads:
+ * FMHA_VARIANT_FOUR_WAVE or FMHA_VARIANT_PINGPONG. Negative sizes give -1.
+ * Host only; makes no HIP call.
+ */
+int32_t fmha_fwd_auto_variant(int32_t batch, int32_t max_seqlen_q, int32_t num_heads);
+
+/*
  * Host-side check of a cu_seqlens array (HOST pointer, batch + 1 entries):
  * starts at 0, is non-decreasing, ends at total, and no document is longer
  * than max_seqlen. Returns FMHA_OK or FMHA_ERR_INVALID_ARG. Makes no HIP call.

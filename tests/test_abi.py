@@ -24,7 +24,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["fmha_fwd", "fmha_fwd_fp8pv", "fmha_fwd_variant",
-                            "fmha_fwd_fp8pv_variant", "fmha_validate_cu_seqlens",
+                            "fmha_fwd_fp8pv_variant", "fmha_fwd_auto_variant",
+                            "fmha_validate_cu_seqlens",
                             "fmha_status_string", "fmha_abi_version"])
 
 
@@ -91,6 +92,26 @@ def test_variant_must_be_known():
     fargs = [0x10000, 0x20000, 0x30000, 0x70000, None, None, 1, 128, 128, 128, 128, 2, 128, 0,
              ctypes.c_float(0.125), 0x40000, 0x50000]
     assert lib.fmha_fwd_fp8pv_variant(*fargs, 7, None) == 1
+
+
+@pytest.mark.parametrize("batch,max_q,heads,want", [
+    (8, 4096, 32, "pingpong"),     # 16 blocks of 256 rows x 8 docs x 32 heads = 4096
+    (1, 32768, 16, "pingpong"),    # 2048 blocks
+    (4, 2048, 32, "pingpong"),     # exactly 1024
+    (1, 2225, 16, "four_wave"),    # 9 x 16 = 144 blocks
+    (1, 8192, 16, "pingpong"),     # 32 x 16 = 512, the threshold
+    (1, 8191, 15, "four_wave"),    # 480
+    (0, 0, 1, "four_wave"),
+])
+def test_auto_variant(batch, max_q, heads, want):
+    import head_attention_forward_fmha_amd as fm
+    assert fm.auto_variant(batch, max_q, heads) == want
+
+
+def test_auto_variant_rejects_negative_sizes():
+    import head_attention_forward_fmha_amd as fm
+    with pytest.raises(ValueError):
+        fm.auto_variant(-1, 10, 1)
 
 
 def test_fwd_empty_problem_is_a_no_op():
