@@ -111,8 +111,9 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
  * Kernel variant selection, for testing and tuning. FMHA_VARIANT_AUTO (what
  * fmha_fwd and fmha_fwd_fp8pv use) takes the 8-wave ping-pong kernel when the
  * problem has at least 512 blocks of 256 query rows, else the 4-wave kernel.
- * All variants compute the same function; results may differ in the last bits
- * of rounding (different tiling of the row-sum and the lazy maximum).
+ * All variants compute the same function. They currently run the same per-row
+ * arithmetic in the same key-tile order and give bit-identical results; the ABI
+ * promises only agreement within rounding.
  */
 #define FMHA_VARIANT_AUTO 0
 #define FMHA_VARIANT_FOUR_WAVE 1   /* 4 waves, 128 query rows per workgroup   */
