@@ -43,7 +43,8 @@ MI355X_HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "head_attention_forward_fmha_amd", "csrc")
 KERNEL_SOURCES = ("fmha_fwd_kernel.hip", "fmha_device.h", "fmha_kernel_params.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fmha_fwd_traffic.json")
-KERNEL_NAMES = {"four_wave": "fmha::fmha_fwd_kernel", "pingpong": "fmha::fmha_fwd_pingpong_kernel"}
+KERNEL_NAMES = {"four_wave": "fmha::fmha_fwd_kernel", "pingpong": "fmha::fmha_fwd_pingpong_kernel",
+                "pipelined": "fmha::fmha_fwd_pipe_kernel"}
 # counted FLOP of the oracle sample: about 10-30 s of fp64 numpy on a 16-core host
 CPU_SAMPLE_FLOP = 4e11
 
@@ -61,6 +62,8 @@ def kernel_source_hash() -> str:
 
 
 def kernel_template_name(w, variant):
+    if variant == "pipelined":
+        return f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}>"
     return (f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}, "
             f"{str(w.fp8_pv).lower()}>")
 
@@ -70,8 +73,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=sorted(SHORT) + sorted(SHORT.values()))
-    ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong"],
+    ap.add_argument("--workload", default="c4",
+                    choices=sorted(SHORT) + sorted(SHORT.values()) + ["x_varlen_noncausal_32k"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong", "pipelined"],
                     help="kernel variant (auto picks by problem size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-flop", type=float, default=CPU_SAMPLE_FLOP,
@@ -263,7 +267,8 @@ def main():
         w = WORKLOADS[SHORT.get(args.workload, args.workload)]
         c = summarize_counters(*args.summarize_counters)
         kernel = c["FETCH_SIZE"]["kernel"]
-        variant = "pingpong" if "pingpong" in kernel else "four_wave"
+        variant = ("pingpong" if "pingpong" in kernel else
+                   "pipelined" if "pipe_kernel" in kernel else "four_wave")
         table = {}
         if os.path.exists(TRAFFIC_FILE):
             with open(TRAFFIC_FILE) as f:
@@ -289,13 +294,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from synthetic import WORKLOADS
+    from synthetic import EXTRA_WORKLOADS, WORKLOADS
     import head_attention_forward_fmha_amd as fm
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(1)
     name = SHORT.get(args.workload, args.workload)
-    w = WORKLOADS[name]
+    w = {**WORKLOADS, **EXTRA_WORKLOADS}[name]
     dev = torch.device("cuda:0")
     inp, d = device_inputs(w, dev)
     step = make_step(w, d, args.variant)

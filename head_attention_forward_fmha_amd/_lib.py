@@ -18,7 +18,7 @@ FMHA_ERR_INVALID_ARG = 1
 FMHA_ERR_UNSUPPORTED = 2
 FMHA_ERR_LAUNCH = 3
 
-VARIANTS = {"auto": 0, "four_wave": 1, "pingpong": 2}
+VARIANTS = {"auto": 0, "four_wave": 1, "pingpong": 2, "pipelined": 3}
 
 EXPORTED_SYMBOLS = (
     "fmha_fwd",

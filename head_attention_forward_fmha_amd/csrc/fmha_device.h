@@ -171,16 +171,61 @@ struct WorkItem {
   int head, q_start, k_start, sq, sk, m0;
 };
 
-// Workgroups are dealt to the 8 XCDs round-robin (id % 8). Work items are
-// ordered (document, head)-major with query blocks inner, longest causal block
-// first, and each XCD takes one contiguous range of them, so the query blocks
-// that stream the same K/V run together on one XCD and share its L2.
-__device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int bm) {
-  const int n_items = p.batch * p.heads * p.n_mblocks;
-  const int wg = blockIdx.x;
-  const int xcd = wg % kXcds;
-  const int per = n_items / kXcds, extra = n_items % kXcds;
-  const int item = xcd * per + min(xcd, extra) + wg / kXcds;
+// Work items are the (document, head, query block) triples, ordered
+// (document, head)-major with query blocks inner, longest causal block first,
+// and split into kXcds contiguous ranges, one per XCD. Workgroups are dealt to
+// the XCDs round-robin (id % kXcds), so the query blocks that stream the same
+// K/V run together on one XCD and share its L2.
+//
+// The kernels are persistent: the launcher sizes the grid to what the chip
+// holds at once (a multiple of kXcds), and the W workgroups of an XCD walk its
+// range in rounds of W items, alternating direction every round, so that a
+// workgroup that drew a long causal block in one round draws a short one in
+// the next and the XCD finishes evenly.
+struct ItemCursor {
+  int start, count, per_xcd, lane, round;
+  __device__ __forceinline__ explicit ItemCursor(const FwdParams& p) {
+    const int n_items = p.batch * p.heads * p.n_mblocks;
+    const int xcd = blockIdx.x % kXcds;
+    const int per = n_items / kXcds, extra = n_items % kXcds;
+    start = xcd * per + min(xcd, extra);
+    count = per + (xcd < extra ? 1 : 0);
+    per_xcd = gridDim.x / kXcds;
+    lane = blockIdx.x / kXcds;
+    round = 0;
+  }
+  // the next item of this workgroup; false when its share is done
+  __device__ __forceinline__ bool next(int& item) {
+    while (round * per_xcd < count) {
+      const int pos = round * per_xcd + ((round & 1) ? per_xcd - 1 - lane : lane);
+      ++round;
+      if (pos < count) {
+        item = start + pos;
+        return true;
+      }
+    }
+    return false;
+  }
+};
+
+// Runs f(p, item) for this workgroup's work items. Persistent launches
+// (kPersistent) walk the XCD's range with an ItemCursor, re-reading the
+// parameters per item (kernel_params); the others take the single item their
+// block index names, with the same XCD-contiguous numbering.
+template <bool kPersistent, typename F>
+__device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f);
+
+// The kernel's own FwdParams argument, read from the kernel-argument segment.
+// The persistent kernels fetch it afresh for every work item: the pointer passes
+// through an empty asm, so the compiler reloads the (invariant) fields where it
+// needs them instead of keeping all of them in scalar registers across the loop.
+__device__ __forceinline__ const FwdParams& kernel_params() {
+  const FwdParams* q = (const FwdParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return *q;
+}
+
+__device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int bm, int item) {
   const int pair = item / p.n_mblocks;
   const int mblock = p.n_mblocks - 1 - (item - pair * p.n_mblocks);
   const int doc = pair / p.heads;
@@ -202,6 +247,27 @@ __device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int bm)
   w.sk = k_end - w.k_start;
   w.m0 = mblock * bm;
   return w;
+}
+
+template <bool kPersistent, typename F>
+__device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f) {
+  if constexpr (kPersistent) {
+    ItemCursor cursor(params);
+    int item;
+    bool first = true;
+    while (cursor.next(item)) {
+      // the previous item ended behind a barrier; this one keeps its epilogue
+      // apart from the next item's first copies
+      if (!first) __syncthreads();
+      first = false;
+      f(kernel_params(), item);
+    }
+  } else {
+    const int n_items = params.batch * params.heads * params.n_mblocks;
+    const int xcd = blockIdx.x % kXcds;
+    const int per = n_items / kXcds, extra = n_items % kXcds;
+    f(params, xcd * per + min(xcd, extra) + (int)blockIdx.x / kXcds);
+  }
 }
 
 // ---------------------------------------------------------------- per-wave tile math
@@ -332,18 +398,41 @@ struct WaveTile {
     }
   }
 
+  // Byte offset of a tile in the copy descriptors' buffers. It is uniform; the
+  // persistent (causal) kernels say so explicitly, which keeps it in a scalar
+  // register there (the buffer loads take it only from one).
+  __device__ __forceinline__ static int scalar_offset(int off) {
+    if constexpr (kCausal) return __builtin_amdgcn_readfirstlane(off);
+    return off;
+  }
+
+  // The copy descriptors are uniform by construction; readfirstlane tells the
+  // compiler so, which keeps them in scalar registers (the buffer loads take
+  // them only there).
+  __device__ __forceinline__ void pin_copy_state() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k_rsrc[i] = __builtin_amdgcn_readfirstlane(k_rsrc[i]);
+      v_rsrc[i] = __builtin_amdgcn_readfirstlane(v_rsrc[i]);
+    }
+    k_stride = __builtin_amdgcn_readfirstlane(k_stride);
+    v_stride = __builtin_amdgcn_readfirstlane(v_stride);
+  }
+
   // This wave's share of the copy of K tile j into K stage kStage (lds_k0 is
   // the LDS address of this wave's first 1 KB block in stage 0): instruction r
   // of kLoadsPerWave, or all of them. V likewise.
   template <int kStage, int kR>
   __device__ __forceinline__ void copy_k_one(int j, uint32_t lds_k0) {
     lds_dma_16<kStage * kTileBytes + 1024 * kWaves * kR>(
-        lds_k0, k_voff[kR], k_rsrc, (int)((uint32_t)(j * kBN) * k_stride));
+        lds_k0, k_voff[kR], k_rsrc,
+        scalar_offset((int)((uint32_t)(j * kBN) * k_stride)));
   }
   template <int kStage, int kR>
   __device__ __forceinline__ void copy_v_one(int j, uint32_t lds_v0) {
     lds_dma_16<kStage * kVTileBytes + 1024 * kWaves * kR>(
-        lds_v0, v_voff[kR], v_rsrc, (int)((uint32_t)(j * kBN) * v_stride));
+        lds_v0, v_voff[kR], v_rsrc,
+        scalar_offset((int)((uint32_t)(j * kBN) * v_stride)));
   }
   template <int kStage>
   __device__ __forceinline__ void copy_k(int j, uint32_t lds_k0) {
@@ -587,6 +676,172 @@ struct WaveTile {
                                                                    0, 127);
       }
     }
+  }
+
+  // ---------------------------------------------------------------- software pipeline (bf16)
+  //
+  // The pipelined kernel walks the keys in half-tiles of 32 (u = 0, 1, ...).
+  // Step u of a wave runs three independent pieces of work as one instruction
+  // stream: the softmax of half-tile u (VALU), S of half-tile u+1 (Q.K^T MFMAs)
+  // and O += P V of half-tile u-1 (P.V MFMAs). A wave thereby keeps its own
+  // matrix-core work in flight while it computes exponentials, instead of
+  // relying on another wave's opposite phase. S and P of consecutive
+  // half-tiles alternate between two register sets (index u & 1). A rescale
+  // of O that the softmax of half-tile u asks for (alpha_o) is applied at the
+  // start of step u+1, after the P.V of half-tile u-1 and before that of u.
+  static constexpr int kHalfQk = kKSteps;        // Q.K^T MFMAs per half-tile
+  static constexpr int kHalfPv = 2 * kDBlocks;   // P.V MFMAs per half-tile
+  f32x16 hs[2];        // S^T of a half-tile: keys 8*(i/4) + 4*half + i%4 for register i
+  bf16x8 hp[2][2];     // bf16 P of a half-tile, per 16-key step
+  float alpha_o;       // pending O rescale (1: none)
+
+  // S^T of the half kH of the K tile at ks, into s.
+  template <int kH>
+  __device__ __forceinline__ void qk_half(const char* ks, f32x16& s) {
+    bf16x8 ka[3];
+    auto rk = [&](int t) { ka[t % 3] = *(const bf16x8*)(ks + k_off[t] + kH * 32 * kRowBytes); };
+    rk(0);
+    if (kHalfQk > 1) rk(1);
+#pragma unroll
+    for (int t = 0; t < kHalfQk; ++t) {
+      if (t + 2 < kHalfQk) rk(t + 2);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qreg[t], t == 0 ? f32x16{} : s, 0, 0, 0);
+    }
+  }
+
+  // The transposed V operand of P.V MFMA t of half kH of the V tile at vs.
+  template <int kH>
+  __device__ __forceinline__ bf16x8 read_v_half(const char* vs, int t) const {
+    const int l = t / kDBlocks, db = t % kDBlocks;
+    const int row0 = 16 * (2 * kH + l);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (LDS_AS bf16x4*)(vs + v_off[0][db] + row0 * kVRowBytes));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (LDS_AS bf16x4*)(vs + v_off[1][db] + row0 * kVRowBytes));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+
+  // O^T += V^T P^T for the half kH of the V tile at vs.
+  template <int kH>
+  __device__ __forceinline__ void pv_half(const char* vs, const bf16x8 (&p)[2]) {
+    bf16x8 va[3];
+    va[0] = read_v_half<kH>(vs, 0);
+    va[1] = read_v_half<kH>(vs, 1);
+#pragma unroll
+    for (int t = 0; t < kHalfPv; ++t) {
+      if (t + 2 < kHalfPv) va[(t + 2) % 3] = read_v_half<kH>(vs, t + 2);
+      oacc[t % kDBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          va[t % 3], p[t / kDBlocks], oacc[t % kDBlocks], 0, 0, 0);
+    }
+  }
+
+  // Causal mask and key tail of half-tile u, if any of its keys needs it.
+  __device__ __forceinline__ void mask_half(f32x16& s, int u, int sk, int causal_off) const {
+    const int k0 = 32 * u;
+    const bool need = (k0 + 32 > sk) || (kCausal && (k0 + 31 > wave_q0 + causal_off));
+    if (need) {
+      const int lim = kCausal ? min(sk - 1, qi + causal_off) : sk - 1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (k0 + 8 * (i / 4) + 4 * half + (i % 4) > lim) s[i] = -__builtin_inff();
+    }
+  }
+
+  // p = exp2(fma(s, c, -c*m_run)) of a half-tile, its bf16 P and this lane's
+  // partial row sum (fp32 p, four chains).
+  __device__ __forceinline__ float exp_half(const f32x16& s, bf16x8 (&p)[2]) const {
+    const float neg_mc = (m_run == -__builtin_inff()) ? 0.f : -m_run * c;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, neg_mc));
+      rs[i & 3] += e;
+      p[i / 8][i % 8] = (bf16_t)e;
+    }
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  }
+
+  // The lazy-maximum check of a half-tile whose p were computed with m_run
+  // (see softmax_lazy): rows whose p exceed 2^8, or that have no maximum yet,
+  // take the tile's row maximum, and their p, l and pending O rescale follow.
+  __device__ __forceinline__ void settle_half(const f32x16& s, bf16x8 (&p)[2], float lane_sum) {
+    const bool raise = (m_run == -__builtin_inff()) || !(lane_sum <= kLazyLimit);
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(raise);
+    if (mask != 0) {
+      const uint32_t rows = (uint32_t)mask | (uint32_t)(mask >> 32);
+      const bool row_raise = (rows >> col) & 1u;
+      float mp[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], s[i]);
+      const float mx = wave_half_swap_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+      const bool up = row_raise && (mx > m_run);
+      const float alpha = up ? __builtin_amdgcn_exp2f((m_run - mx) * c) : 1.f;
+      m_run = up ? mx : m_run;
+      l_run *= alpha;
+      alpha_o *= alpha;
+      lane_sum = exp_half(s, p);
+    }
+    l_run += lane_sum;
+  }
+
+  // Apply a pending rescale of O (all P.V MFMAs issued so far must have landed).
+  __device__ __forceinline__ void settle_o() {
+    if (__builtin_amdgcn_ballot_w64(alpha_o != 1.f) != 0) {
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha_o;
+      alpha_o = 1.f;
+    }
+  }
+
+  // Steady-state step u (kPar = u & 1) as one interleaved stream: softmax of
+  // hs[kPar] into hp[kPar]; S of half-tile u+1 (half kPar^1 of the K tile at
+  // ks) into hs[kPar^1]; O += P V of half-tile u-1 (hp[kPar^1], half kPar^1 of
+  // the V tile at vs). Returns this lane's partial row sum of half-tile u.
+  template <int kPar>
+  __device__ __forceinline__ float step_interleaved(const char* ks, const char* vs) {
+    constexpr int kH = kPar ^ 1;
+    static_assert(kHalfQk == kHalfPv, "Q.K^T and P.V steps pair up one to one");
+    constexpr int kN = kHalfQk;
+    bf16x8 ka[3], va[3];
+    auto rk = [&](int t) { ka[t % 3] = *(const bf16x8*)(ks + k_off[t] + kH * 32 * kRowBytes); };
+    const float neg_mc = (m_run == -__builtin_inff()) ? 0.f : -m_run * c;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    rk(0);
+    va[0] = read_v_half<kH>(vs, 0);
+    rk(1);
+    va[1] = read_v_half<kH>(vs, 1);
+#pragma unroll
+    for (int t = 0; t < kN; ++t) {
+      if (t + 2 < kN) {
+        rk(t + 2);
+        va[(t + 2) % 3] = read_v_half<kH>(vs, t + 2);
+      }
+      hs[kH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qreg[t],
+                                                       t == 0 ? f32x16{} : hs[kH], 0, 0, 0);
+      oacc[t % kDBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          va[t % 3], hp[kH][t / kDBlocks], oacc[t % kDBlocks], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(hs[kPar][i], c, neg_mc));
+      rs[i & 3] += e;
+      hp[kPar][i / 8][i % 8] = (bf16_t)e;
+    }
+    // order: the first two steps' operand reads; then per step its reads two
+    // steps ahead, each MFMA followed by a share of the softmax arithmetic
+    constexpr int kValuPerMfma = (56 + 2 * kN - 1) / (2 * kN);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int t = 0; t < kN; ++t) {
+      if (t + 2 < kN) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+    }
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
   }
 
   // O /= l -> bf16 store; LSE = scale*m + ln(l) (natural log). A row with no

@@ -19,9 +19,12 @@
 //    tiles are shared by 256 query rows (half the LDS and L2 traffic per
 //    FLOP of the 4-wave kernel).
 //
-// Both kernels take their work item from an XCD-aware remap of the 1-D grid
-// (decode_work_item) and stream K/V tiles of 64 keys through a double buffer
+// Causal launches are persistent (each workgroup walks its XCD's share of the
+// work items, see for_each_item); every kernel streams K/V tiles of 64 keys through a double buffer
 // with buffer_load ... lds copies ordered by explicit vmcnt waits and barriers.
+
+#include <algorithm>
+#include <atomic>
 
 #include "fmha_device.h"
 
@@ -36,13 +39,14 @@ static_assert(kBM4 == kRowsFourWave, "4-wave block height");
 template <int kD, bool kCausal, bool kFp8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves4 * 64, kWaves4 * 64),
                           amdgpu_waves_per_eu(2, 2)))
-void fmha_fwd_kernel(FwdParams p) {
+void fmha_fwd_kernel(FwdParams params) {
   using WT = WaveTile<kD, kCausal, kFp8, kWaves4>;
   __shared__ __attribute__((aligned(1024))) char smem_k[2][WT::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char smem_v[2][WT::kVTileBytes];
 
-  const WorkItem w = decode_work_item(p, kBM4);
-  if (w.m0 >= w.sq) return;  // uniform over the workgroup, before any barrier
+  auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
+  const WorkItem w = decode_work_item(p, kBM4, item);
+  if (w.m0 >= w.sq) return;  // uniform over the workgroup
   const int causal_off = w.sk - w.sq;
   int kend = w.sk;
   if (kCausal) kend = min(w.sk, max(0, w.m0 + kBM4 + causal_off));
@@ -51,6 +55,7 @@ void fmha_fwd_kernel(FwdParams p) {
   const int wave = threadIdx.x >> 6;
   WT t;
   t.init(p, w, wave, wave);
+  t.pin_copy_state();
   const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * wave]);
   const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * wave]);
 
@@ -88,6 +93,8 @@ void fmha_fwd_kernel(FwdParams p) {
   if (j < n_tiles) step(j, std::integral_constant<int, 0>());
 
   t.epilogue(p, w);
+  };
+  for_each_item<kCausal>(params, run_item);
 }
 
 // ---------------------------------------------------------------- 8-wave ping-pong kernel
@@ -107,15 +114,16 @@ struct NoPhaseTrace {
 template <int kD, bool kCausal, bool kFp8, typename Trace = NoPhaseTrace>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves8 * 64, kWaves8 * 64),
                           amdgpu_waves_per_eu(2, 2)))
-void fmha_fwd_pingpong_kernel(FwdParams p) {
+void fmha_fwd_pingpong_kernel(FwdParams params) {
   // each group of 4 waves copies whole tiles, so the tile math is set up for 4
   // copying waves
   using WT = WaveTile<kD, kCausal, kFp8, 4>;
   __shared__ __attribute__((aligned(1024))) char smem_k[kStages8][WT::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char smem_v[kStages8][WT::kVTileBytes];
 
-  const WorkItem w = decode_work_item(p, kBM8);
-  if (w.m0 >= w.sq) return;  // uniform over the workgroup, before any barrier
+  auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
+  const WorkItem w = decode_work_item(p, kBM8, item);
+  if (w.m0 >= w.sq) return;  // uniform over the workgroup
   const int causal_off = w.sk - w.sq;
   int kend = w.sk;
   if (kCausal) kend = min(w.sk, max(0, w.m0 + kBM8 + causal_off));
@@ -126,6 +134,7 @@ void fmha_fwd_pingpong_kernel(FwdParams p) {
   // 32-row chunks alternate between the groups, which evens out the causal work
   WT t;
   t.init(p, w, wave & 3, 2 * (wave & 3) + grp);
+  if constexpr (kCausal) t.pin_copy_state();
   const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * (wave & 3)]);
   const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * (wave & 3)]);
   Trace trace;
@@ -210,24 +219,172 @@ void fmha_fwd_pingpong_kernel(FwdParams p) {
   if (j + 1 <= n) slot_pair(j + 1, std::integral_constant<int, 1>());
 
   t.epilogue(p, w);
+  };
+  for_each_item<kCausal>(params, run_item);
+}
+
+// ---------------------------------------------------------------- pipelined kernel
+
+// 4 waves (128 query rows) per workgroup, two workgroups per CU, bf16 only.
+// Each wave software-pipelines its own work over half-tiles of 32 keys (see
+// WaveTile::step_interleaved): iteration i (one barrier) runs steps 2i-1 and
+// 2i, which read K tile i (Q.K^T of half-tiles 2i and 2i+1) and V tile i-1
+// (P.V of half-tiles 2i-2 and 2i-1), while the copies of K tile i+1 and V
+// tile i fill the other LDS stages.
+constexpr int kWavesPipe = 4;
+constexpr int kBMPipe = kWavesPipe * 32;
+static_assert(kBMPipe == kRowsPipelined, "pipelined block height");
+
+template <int kD, bool kCausal>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWavesPipe * 64, kWavesPipe * 64),
+                          amdgpu_waves_per_eu(2, 2)))
+void fmha_fwd_pipe_kernel(FwdParams params) {
+  using WT = WaveTile<kD, kCausal, false, kWavesPipe>;
+  __shared__ __attribute__((aligned(1024))) char smem_k[2][WT::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_v[2][WT::kVTileBytes];
+
+  auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
+  const WorkItem w = decode_work_item(p, kBMPipe, item);
+  if (w.m0 >= w.sq) return;  // uniform over the workgroup
+  const int causal_off = w.sk - w.sq;
+  int kend = w.sk;
+  if (kCausal) kend = min(w.sk, max(0, w.m0 + kBMPipe + causal_off));
+  const int n_half = (kend + 31) / 32;
+  const int n_tiles = (kend + kBN - 1) / kBN;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WT t;
+  t.init(p, w, wave, wave);
+  t.pin_copy_state();
+  t.alpha_o = 1.f;
+  const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * wave]);
+  const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * wave]);
+
+  // copies of iteration i: K tile i+1 and V tile i (stage i % 2 each); they
+  // land before iteration i+1
+  auto copies = [&](int i) __attribute__((always_inline)) {
+    const uint32_t kst1 = (uint32_t)((i + 1) & 1), vst = (uint32_t)(i & 1);
+    if (i + 1 < n_tiles)
+      t.template copy_k<0>(i + 1, __builtin_amdgcn_readfirstlane(k_lds0 + kst1 * WT::kTileBytes));
+    if (i < n_tiles)
+      t.template copy_v<0>(i, __builtin_amdgcn_readfirstlane(v_lds0 + vst * WT::kVTileBytes));
+  };
+  auto finish_iteration = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+  };
+  // a step with a piece missing (the first and last ones): the pieces run one
+  // after another
+  auto step_general = [&](int u, auto par_tag, const char* ks, const char* vs)
+                          __attribute__((always_inline)) {
+    constexpr int par = decltype(par_tag)::value;
+    constexpr int h = par ^ 1;
+    t.settle_o();
+    if (u >= 1 && u - 1 < n_half) t.template pv_half<h>(vs, t.hp[h]);
+    if (u + 1 < n_half) t.template qk_half<h>(ks, t.hs[h]);
+    if (u >= 0 && u < n_half) {
+      t.mask_half(t.hs[par], u, w.sk, causal_off);
+      const float ls = t.exp_half(t.hs[par], t.hp[par]);
+      t.settle_half(t.hs[par], t.hp[par], ls);
+    }
+  };
+  // iteration i reads K tile i (stage i % 2) and V tile i-1 (the other stage)
+  auto iteration_general = [&](int i) __attribute__((always_inline)) {
+    copies(i);
+    const char* ks = smem_k[i & 1];
+    const char* vs = smem_v[(i & 1) ^ 1];
+    step_general(2 * i - 1, std::integral_constant<int, 1>(), ks, vs);
+    step_general(2 * i, std::integral_constant<int, 0>(), ks, vs);
+    finish_iteration();
+  };
+  // steady state: both steps have all three pieces
+  auto iteration_steady = [&](int i, auto kstage_tag) __attribute__((always_inline)) {
+    constexpr int kst = decltype(kstage_tag)::value;  // i % 2
+    copies(i);
+    t.settle_o();
+    t.mask_half(t.hs[1], 2 * i - 1, w.sk, causal_off);
+    float ls = t.template step_interleaved<1>(smem_k[kst], smem_v[kst ^ 1]);
+    t.settle_half(t.hs[1], t.hp[1], ls);
+    t.settle_o();
+    t.mask_half(t.hs[0], 2 * i, w.sk, causal_off);
+    ls = t.template step_interleaved<0>(smem_k[kst], smem_v[kst ^ 1]);
+    t.settle_half(t.hs[0], t.hp[0], ls);
+    finish_iteration();
+  };
+
+  if (n_tiles > 0) {
+    t.template copy_k<0>(0, k_lds0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    // iterations 0 .. ceil(n_half / 2); the last one holds the final P.V.
+    // Iterations 1 .. last_steady have every piece of both steps.
+    const int n_iter = (n_half + 1) / 2 + 1;
+    const int last_steady = (n_half - 2) / 2;
+    iteration_general(0);
+    int i = 1;
+    for (; i + 1 <= last_steady; i += 2) {
+      iteration_steady(i, std::integral_constant<int, 1>());
+      iteration_steady(i + 1, std::integral_constant<int, 0>());
+    }
+    if (i <= last_steady) {
+      iteration_steady(i, std::integral_constant<int, 1>());
+      ++i;
+    }
+    for (; i < n_iter; ++i) iteration_general(i);
+  }
+
+  t.epilogue(p, w);
+  };
+  for_each_item<kCausal>(params, run_item);
 }
 
 // ---------------------------------------------------------------- launchers
 
+// Compute units of the current device (cached per device; the attribute query
+// is a host call).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 template <int kD, bool kCausal, bool kFp8>
 static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   FwdParams q = p;
-  const bool use8 = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads) == kVariantPingPong;
+  const int variant_run = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads, kFp8);
+  const bool use8 = variant_run == kVariantPingPong;
   const int bm = use8 ? kBM8 : kBM4;
   q.n_mblocks = (p.max_seqlen_q + bm - 1) / bm;
   const long long n_items = (long long)q.n_mblocks * p.heads * p.batch;
   if (n_items == 0) return hipSuccess;
   if (n_items > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (use8)
-    hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<kD, kCausal, kFp8>), dim3((unsigned)n_items),
+  // causal kernels are persistent: as many workgroups as the chip holds at once
+  // (one per CU for the 8-wave kernel, two for the 4-wave ones), a multiple of
+  // the XCD count; the others take one item per workgroup
+  const long long resident = (long long)device_cus() * (use8 ? 1 : 2);
+  const long long grid =
+      kCausal ? (std::min(n_items, resident) + kXcds - 1) / kXcds * kXcds : n_items;
+  if (variant_run == kVariantPipelined) {
+    if constexpr (!kFp8)
+      hipLaunchKernelGGL((fmha_fwd_pipe_kernel<kD, kCausal>), dim3((unsigned)grid),
+                         dim3(kWavesPipe * 64), 0, stream, q);
+    else
+      return hipErrorInvalidValue;
+  } else if (use8)
+    hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<kD, kCausal, kFp8>), dim3((unsigned)grid),
                        dim3(kWaves8 * 64), 0, stream, q);
   else
-    hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kFp8>), dim3((unsigned)n_items),
+    hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kFp8>), dim3((unsigned)grid),
                        dim3(kWaves4 * 64), 0, stream, q);
   return hipGetLastError();
 }

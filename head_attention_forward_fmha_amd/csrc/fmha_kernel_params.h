@@ -30,19 +30,24 @@ struct FwdParams {
 constexpr int kVariantAuto = 0;      // pick by problem size
 constexpr int kVariantFourWave = 1;  // 4 waves, 128 query rows per workgroup
 constexpr int kVariantPingPong = 2;  // 8 waves in two phase-shifted groups, 256 rows
+constexpr int kVariantPipelined = 3; // 4 waves, each software-pipelined (bf16 only)
 
 // Query rows per workgroup of each kernel.
 constexpr int kRowsFourWave = 128;
 constexpr int kRowsPingPong = 256;
+constexpr int kRowsPipelined = 128;
 
 // The kernel a launch runs. Automatic selection takes the 8-wave kernel once the
-// problem has at least 512 blocks of 256 query rows (two per CU), else the
-// 4-wave kernel, whose smaller blocks fill the chip better on small problems.
-inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int32_t heads) {
+// problem has at least 128 blocks of 256 query rows (half the CUs of an
+// MI355X), else the 4-wave kernel, whose smaller blocks spread a small problem
+// over more CUs.
+inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int32_t heads,
+                           bool fp8 = false) {
+  (void)fp8;
   if (variant != kVariantAuto) return variant;
   const long long blocks = ((long long)max_seqlen_q + kRowsPingPong - 1) / kRowsPingPong *
                            heads * batch;
-  return blocks >= 512 ? kVariantPingPong : kVariantFourWave;
+  return blocks >= 128 ? kVariantPingPong : kVariantFourWave;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, int variant,

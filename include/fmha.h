@@ -110,7 +110,7 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
 /*
  * Kernel variant selection, for testing and tuning. FMHA_VARIANT_AUTO (what
  * fmha_fwd and fmha_fwd_fp8pv use) takes the 8-wave ping-pong kernel when the
- * problem has at least 512 blocks of 256 query rows, else the 4-wave kernel.
+ * problem has at least 128 blocks of 256 query rows, else the 4-wave kernel.
  * All variants compute the same function. They currently run the same per-row
  * arithmetic in the same key-tile order and give bit-identical results; the ABI
  * promises only agreement within rounding.
@@ -118,6 +118,8 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
 #define FMHA_VARIANT_AUTO 0
 #define FMHA_VARIANT_FOUR_WAVE 1   /* 4 waves, 128 query rows per workgroup   */
 #define FMHA_VARIANT_PINGPONG 2    /* 8 waves in two phase-shifted groups     */
+#define FMHA_VARIANT_PIPELINED 3   /* 4 waves, each software-pipelined; bf16
+                                      only (fp8 P.V: FMHA_ERR_UNSUPPORTED)   */
 
 /* fmha_fwd with an explicit kernel variant (any other value: INVALID_ARG). */
 fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,

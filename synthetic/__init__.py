@@ -119,6 +119,14 @@ WORKLOADS = {
         heads=16, head_dim=128, causal=True, doc_lens=_linspace_docs(32768, 1), fp8_pv=True),
 }
 
+# Extra shapes for measurement only (not among the five above): the c4 token
+# layout without the causal mask, which isolates the cost of causal scheduling.
+EXTRA_WORKLOADS = {
+    "x_varlen_noncausal_32k": Workload(
+        "x_varlen_noncausal_32k", "varlen non-causal: 32768 tokens / 8 docs, h=32 d=128",
+        heads=32, head_dim=128, causal=False, doc_lens=_linspace_docs(32768, 8)),
+}
+
 
 def cu_seqlens(lens) -> tuple:
     """(cu_q, cu_k) int32 prefix sums of per-document (sq, sk) lengths."""

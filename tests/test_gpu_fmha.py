@@ -23,7 +23,8 @@ from synthetic import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["four_wave", "pingpong"]
+VARIANTS = ["four_wave", "pingpong", "pipelined"]
+VARIANTS_FP8 = ["four_wave", "pingpong"]   # the pipelined kernel is bf16 only
 
 O_ATOL = O_RTOL = 1e-2
 O_ATOL_FP8 = O_RTOL_FP8 = 5e-2
@@ -104,9 +105,10 @@ def _sample_rows(cu, heads, n_random, seed):
     return sorted(s)
 
 
-def _sampled_parity(w, n_random=1500, seed=0):
+def _sampled_parity(w, n_random=1500, seed=0, variant="auto"):
     inp = workload_inputs(w)
-    o, lse = _run(inp, w.causal, w.softmax_scale, w.heads, w.head_dim, fp8=w.fp8_pv)
+    o, lse = _run(inp, w.causal, w.softmax_scale, w.heads, w.head_dim, fp8=w.fp8_pv,
+                  variant=variant)
     samples = _sample_rows(inp.cu_q, w.heads, n_random, seed)
     if w.fp8_pv:
         o_ref, l_ref = oracle.attention_fp8pv_sampled(inp.q, inp.k, inp.v_e4m3, inp.v_scale,
@@ -153,12 +155,19 @@ def test_c2_dense_layout_matches_packed():
     assert torch.equal(l1, l2)
 
 
-def test_c3_varlen_causal_8k_sampled():
-    _sampled_parity(WORKLOADS["c3_varlen_causal_8k"])
+@pytest.mark.parametrize("variant", ["auto", "pipelined"])
+def test_c3_varlen_causal_8k_sampled(variant):
+    _sampled_parity(WORKLOADS["c3_varlen_causal_8k"], variant=variant)
 
 
-def test_c4_varlen_causal_32k_sampled():
-    _sampled_parity(WORKLOADS["c4_varlen_causal_32k"], n_random=1000)
+@pytest.mark.parametrize("variant", ["auto", "pipelined"])
+def test_c4_varlen_causal_32k_sampled(variant):
+    _sampled_parity(WORKLOADS["c4_varlen_causal_32k"], n_random=1000, variant=variant)
+
+
+def test_c2_dense_2225_pipelined():
+    w = WORKLOADS["c2_dense_2225"]
+    _full_parity(w.doc_lens, w.heads, w.head_dim, w.causal, variant="pipelined")
 
 
 def test_c5_causal_fp8pv_32k_sampled():
@@ -196,7 +205,7 @@ def test_many_small_documents(variant):
         _full_parity(lens, 4, 128, causal, seed=11, variant=variant)
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS_FP8)
 def test_fp8_small_cases(variant):
     for lens, causal in ((((200, 200),), True), (((129, 129), (64, 64)), False),
                          (((100, 300), (300, 100)), True), (((600, 600), (1, 1)), True)):
@@ -220,7 +229,9 @@ def test_max_seqlen_larger_than_needed(variant):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("fp8", [False, True])
 def test_kernel_variants_agree_bitwise(causal, fp8):
-    """Both kernels run the same per-row arithmetic in the same tile order."""
+    """The 4-wave and ping-pong kernels run the same per-row arithmetic in the
+    same tile order (the pipelined kernel checks its maximum per 32 keys, so it
+    agrees with them only within rounding)."""
     lens = ((1000, 1000), (333, 333), (1, 1), (700, 701))
     inp = make_inputs(lens, 4, 128, seed=29, fp8_pv=fp8)
     scale = float(np.float32(1.0 / np.sqrt(128)))
@@ -231,59 +242,73 @@ def test_kernel_variants_agree_bitwise(causal, fp8):
 
 # ---------------------------------------------------------------- bitwise properties
 
-def test_deterministic_repeats():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_deterministic_repeats(variant):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     inp = make_inputs(((1000, 1000), (777, 777)), 8, 128, seed=21)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     cq = torch.from_numpy(inp.cu_q).to(dev)
-    ref_o, ref_l = fm.fwd(q, k, v, cq, cq, 1000, 1000, causal=True)
+    ref_o, ref_l = fm.fwd(q, k, v, cq, cq, 1000, 1000, causal=True, variant=variant)
     for _ in range(20):
-        o, l = fm.fwd(q, k, v, cq, cq, 1000, 1000, causal=True)
+        o, l = fm.fwd(q, k, v, cq, cq, 1000, 1000, causal=True, variant=variant)
         assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
 
 
-def test_causal_future_keys_do_not_leak():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_causal_future_keys_do_not_leak(variant):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     inp = make_inputs(((500, 500),), 4, 128, seed=23)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     cq = torch.from_numpy(inp.cu_q).to(dev)
-    o1, l1 = fm.fwd(q, k, v, cq, cq, 500, 500, causal=True)
+    o1, l1 = fm.fwd(q, k, v, cq, cq, 500, 500, causal=True, variant=variant)
     i = 200
     k2, v2 = k.clone(), v.clone()
     k2[i + 1:] = k2[i + 1:] * 3 + 1
     v2[i + 1:] = -v2[i + 1:]
-    o2, l2 = fm.fwd(q, k2, v2, cq, cq, 500, 500, causal=True)
+    o2, l2 = fm.fwd(q, k2, v2, cq, cq, 500, 500, causal=True, variant=variant)
     torch.cuda.synchronize()
     assert torch.equal(o1[:i + 1], o2[:i + 1]) and torch.equal(l1[:, :i + 1], l2[:, :i + 1])
     assert not torch.equal(o1[i + 1:], o2[i + 1:])
 
 
-def test_documents_are_isolated_and_match_per_document_calls():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_documents_are_isolated_and_match_per_document_calls(variant):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     lens = ((300, 300), (129, 129), (513, 513))
     inp = make_inputs(lens, 4, 128, seed=25)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     cq = torch.from_numpy(inp.cu_q).to(dev)
-    o, l = fm.fwd(q, k, v, cq, cq, 513, 513, causal=True)
+    o, l = fm.fwd(q, k, v, cq, cq, 513, 513, causal=True, variant=variant)
     for b in range(3):
         a, e = int(inp.cu_q[b]), int(inp.cu_q[b + 1])
-        ob, lb = fm.fwd(q[a:e].contiguous(), k[a:e].contiguous(), v[a:e].contiguous(), causal=True)
+        ob, lb = fm.fwd(q[a:e].contiguous(), k[a:e].contiguous(), v[a:e].contiguous(), causal=True,
+                        variant=variant)
         torch.cuda.synchronize()
         assert torch.equal(ob, o[a:e]) and torch.equal(lb, l[:, a:e])
 
 
-def test_causal_row0_is_v0_exactly():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_causal_row0_is_v0_exactly(variant):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     inp = make_inputs(((64, 64), (200, 200)), 4, 128, seed=27)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     cq = torch.from_numpy(inp.cu_q).to(dev)
-    o, l = fm.fwd(q, k, v, cq, cq, 200, 200, causal=True)
+    o, l = fm.fwd(q, k, v, cq, cq, 200, 200, causal=True, variant=variant)
     torch.cuda.synchronize()
     for a in (0, 64):
         assert torch.equal(o[a], v[a])
         ref = 0.08838834764831845 * (q[a].double().cpu() * k[a].double().cpu()).sum(-1)
         assert torch.allclose(l[:, a].double().cpu(), ref, atol=1e-4, rtol=0)
+
+
+def test_pipelined_rejects_fp8():
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    inp = make_inputs(((128, 128),), 2, 128, seed=31, fp8_pv=True)
+    with pytest.raises(fm.FmhaError):
+        fm.fwd_fp8pv(inp.q.to(dev), inp.k.to(dev), inp.v_e4m3.to(dev), inp.v_scale.to(dev),
+                     variant="pipelined")
