@@ -8,7 +8,9 @@ varlen-causal d=128 case the headline figure is quoted on: 32768 tokens in 8
 documents (cu_seqlens = round(linspace(0, 32768, 9))), 32 heads, seed 0.
 
 Timing follows the FA4 spill issue's protocol (W warm-up steps, then K timed
-steps; GPU events on the stream the kernel runs on). value = counted FLOP of
+steps; GPU events on the stream the kernel runs on). The defaults (30 warm-up,
+100 timed steps) let the GPU clock settle first: the first tens of
+milliseconds after idle run at lower clocks. value = counted FLOP of
 K steps / elapsed time, with FLOP = 4*h*sum(sq*sk)*d halved for causal.
 
 Extra objects on the same line:
@@ -71,8 +73,10 @@ def kernel_template_name(w, variant):
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the GPU's clock ramps up over the first tens of milliseconds of work: the
+    # defaults warm up for about 30 ms of c4 and time about 100 ms
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c4",
                     choices=sorted(SHORT) + sorted(SHORT.values()) + ["x_varlen_noncausal_32k"])
     ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong", "pipelined"],
