@@ -126,8 +126,9 @@ __device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base, uint32_t num
 // HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l
 // writes LDS bytes [lds + 16*l, lds + 16*l + 16). Written as inline asm so that
 // the compiler does not serialise it against unrelated LDS reads; the kernels
-// order it explicitly with s_waitcnt vmcnt + s_barrier. m0 is reserved by the
-// compiler and never holds a live value in these kernels.
+// order it explicitly with s_waitcnt vmcnt + s_barrier. The asm writes m0 and,
+// through s_add_u32, the scalar condition code; both are declared clobbered, as
+// the copies sit between compiler-generated branches.
 template <int kLdsOffset>
 __device__ __forceinline__ void lds_dma_16(uint32_t lds_base, int voffset, i32x4 rsrc,
                                            int soffset) {
@@ -139,7 +140,7 @@ __device__ __forceinline__ void lds_dma_16(uint32_t lds_base, int voffset, i32x4
       "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
       : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset), "n"(kLdsOffset)
-      : "memory");
+      : "memory", "scc", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {

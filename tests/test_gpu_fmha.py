@@ -312,3 +312,19 @@ def test_pipelined_rejects_fp8():
     with pytest.raises(fm.FmhaError):
         fm.fwd_fp8pv(inp.q.to(dev), inp.k.to(dev), inp.v_e4m3.to(dev), inp.v_scale.to(dev),
                      variant="pipelined")
+
+
+# ---------------------------------------------------------------- stale LDS
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_stale_lds_is_never_read(variant, causal, d):
+    """Every LDS byte a pass reads was written by that pass: with the LDS of all
+    CUs filled with NaN bit patterns beforehand, the outputs stay finite and
+    match the oracle (lengths with ragged tiles and several copy rounds)."""
+    from tests.gpu_support import poison_lds
+    dev = _dev()
+    for lens in (((65, 65),), ((130, 130),), ((300, 300), (77, 77))):
+        poison_lds(torch.cuda.current_stream(dev).cuda_stream)
+        _full_parity(lens, 3, d, causal, seed=41, variant=variant)
