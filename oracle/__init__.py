@@ -11,16 +11,29 @@ Parity status per function:
       float8_e4m3fn casts);
   attention_fp8pv -- pinned through its parts (decode + attention);
   attention_fp8pv_emulated -- a diagnostic only; parity unpinned.
+  e2m1_decode / e2m1_encode / mx_dequantize_v -- pinned (the e2m1 value table,
+      agreement with the independently written threshold encoder of the
+      synthetic inputs, nearest-value and scale-rule checks, exact round trips);
+  attention_fp4pv -- pinned through its parts (MX decode + attention);
+  attention_fp4pv_emulated -- pinned (pure-Python brute force, exactness when
+      every scaled P is an e2m1 value, closed forms for a dropped key and a
+      single visible key, the log-domain fold against post-exp division, group
+      locality, and the error bound against attention_fp4pv).
 """
 
 from .reference import (DEFAULT_ROW_BLOCK, attention, attention_bruteforce, attention_rows,
                         attention_sampled, scores, softmax_rows, visible)
 from .fp8 import (E4M3_MAX, attention_fp8pv, attention_fp8pv_emulated, attention_fp8pv_sampled,
                   dequantize_v, e4m3_decode, e4m3_encode)
+from .fp4 import (E2M1_MAX, FP4Emulation, attention_fp4pv, attention_fp4pv_bruteforce,
+                  attention_fp4pv_emulated, attention_fp4pv_sampled, e2m1_decode, e2m1_encode,
+                  mx_dequantize_v)
 
 __all__ = [
     "DEFAULT_ROW_BLOCK", "attention", "attention_bruteforce", "attention_rows",
     "attention_sampled", "scores", "softmax_rows", "visible", "E4M3_MAX", "attention_fp8pv",
     "attention_fp8pv_emulated", "attention_fp8pv_sampled", "dequantize_v", "e4m3_decode",
-    "e4m3_encode",
+    "e4m3_encode", "E2M1_MAX", "FP4Emulation", "attention_fp4pv", "attention_fp4pv_bruteforce",
+    "attention_fp4pv_emulated", "attention_fp4pv_sampled", "e2m1_decode", "e2m1_encode",
+    "mx_dequantize_v",
 ]

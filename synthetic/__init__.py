@@ -18,6 +18,13 @@ scale per head: ``scale[h] = max|V[:, h, :]| / 448`` and
 ``codes = e4m3(clamp(V / scale[h], -448, 448))`` with round-to-nearest-even
 (torch's ``float8_e4m3fn`` cast). This is input preparation for that variant;
 the oracle decodes the codes with its own decoder.
+
+The fp4 P.V workload hands V over in OCP MXFP4 along the token axis: for every
+block of 32 consecutive tokens of the packed tensor, head and d, one E8M0
+exponent X = floor(log2(max|V|)) - 2 (the MX rule for e2m1, whose largest
+exponent is 2; -127 for an all-zero block), and e2m1 codes of V / 2^X rounded
+to nearest, ties to even, saturating at 6. Codes are packed two per byte along
+d (even d in the low nibble); exponents are stored as X + 127.
 """
 
 from __future__ import annotations
@@ -43,6 +50,7 @@ class Workload:
     # True when the tensors are laid out dense [b, s, h, d] (all docs equal).
     dense: bool = False
     fp8_pv: bool = False
+    fp4_pv: bool = False
     seed: int = 0
 
     @property
@@ -77,7 +85,10 @@ class Workload:
     def hbm_bytes(self) -> float:
         """Algorithmic HBM bytes: Q, K, V read once, O written once, LSE written once."""
         h, d = self.heads, self.head_dim
-        v_bytes = 1 if self.fp8_pv else 2
+        if self.fp4_pv:   # e2m1 codes plus one exponent byte per 32 tokens
+            v_bytes = 0.5 + 1.0 / 32.0
+        else:
+            v_bytes = 1 if self.fp8_pv else 2
         return float(self.total_q * h * d * 2 + self.total_k * h * d * (2 + v_bytes)
                      + self.total_q * h * d * 2 + self.total_q * h * 4
                      + (h * 4 if self.fp8_pv else 0))
@@ -120,11 +131,15 @@ WORKLOADS = {
 }
 
 # Extra shapes for measurement only (not among the five above): the c4 token
-# layout without the causal mask, which isolates the cost of causal scheduling.
+# layout without the causal mask, which isolates the cost of causal scheduling,
+# and the c5 shape with P.V in fp4 (MXFP4 V, per-group e2m1 P).
 EXTRA_WORKLOADS = {
     "x_varlen_noncausal_32k": Workload(
         "x_varlen_noncausal_32k", "varlen non-causal: 32768 tokens / 8 docs, h=32 d=128",
         heads=32, head_dim=128, causal=False, doc_lens=_linspace_docs(32768, 8)),
+    "x_causal_fp4pv_32k": Workload(
+        "x_causal_fp4pv_32k", "single-doc causal fp4 P.V: 32768 tokens, h=16 d=128",
+        heads=16, head_dim=128, causal=True, doc_lens=_linspace_docs(32768, 1), fp4_pv=True),
 }
 
 
@@ -149,6 +164,8 @@ class Inputs:
     cu_k: np.ndarray           # int32 [batch + 1]
     v_e4m3: Optional[torch.Tensor] = None   # uint8 [total_k, h, d] (fp8 workloads)
     v_scale: Optional[torch.Tensor] = None  # fp32 [h]
+    v_e2m1: Optional[torch.Tensor] = None   # uint8 [total_k, h, d / 2] (fp4 workloads)
+    v_mx_scale: Optional[torch.Tensor] = None  # uint8 [ceil(total_k / 32), h, d]
     extra: dict = field(default_factory=dict)
 
 
@@ -161,8 +178,46 @@ def quantize_v_e4m3(v: torch.Tensor):
     return codes.view(torch.uint8).contiguous(), scale.contiguous()
 
 
+MX_BLOCK = 32
+
+
+def _e2m1_codes(y: torch.Tensor) -> torch.Tensor:
+    """Nearest e2m1 code of fp32 values, ties to the even code, saturating at 6.
+
+    The thresholds are the midpoints of 0, .5, 1, 1.5, 2, 3, 4, 6; a midpoint
+    belongs to the neighbour with the even code (0, 1, 2, 3, 4, 5, 6, 7 are the
+    codes of those values).
+    """
+    a = y.abs()
+    code = ((a > 0.25).to(torch.uint8) + (a >= 0.75).to(torch.uint8) + (a > 1.25).to(torch.uint8)
+            + (a >= 1.75).to(torch.uint8) + (a > 2.5).to(torch.uint8) + (a >= 3.5).to(torch.uint8)
+            + (a > 5.0).to(torch.uint8))
+    neg = (y < 0) & (code != 0)
+    return torch.where(neg, code | 8, code).to(torch.uint8)
+
+
+def quantize_v_mxfp4(v: torch.Tensor):
+    """MXFP4 along tokens (input preparation for fp4 P.V); see the module docstring.
+
+    Returns (packed codes uint8 [t, h, d/2], exponents uint8 [ceil(t/32), h, d]).
+    """
+    vf = v.float()
+    t, h, d = vf.shape
+    nb = (t + MX_BLOCK - 1) // MX_BLOCK
+    padded = torch.zeros((nb * MX_BLOCK, h, d), dtype=torch.float32)
+    padded[:t] = vf
+    blocks = padded.view(nb, MX_BLOCK, h, d)
+    amax = blocks.abs().amax(dim=1)
+    _, e = torch.frexp(amax)            # amax = f * 2^e with f in [0.5, 1): floor(log2) = e - 1
+    x = torch.where(amax > 0, e - 3, torch.full_like(e, -127)).clamp(-127, 127)
+    y = torch.ldexp(blocks, (-x).unsqueeze(1).to(torch.float32))
+    codes = _e2m1_codes(y).view(nb * MX_BLOCK, h, d)[:t]
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed.contiguous(), (x + 127).to(torch.uint8).contiguous()
+
+
 def make_inputs(lens, heads: int, head_dim: int, seed: int = 0, fp8_pv: bool = False,
-                head_dim_v: Optional[int] = None) -> Inputs:
+                head_dim_v: Optional[int] = None, fp4_pv: bool = False) -> Inputs:
     """Draw q, k, v for documents with per-doc (sq, sk) lengths ``lens``."""
     dv = head_dim if head_dim_v is None else head_dim_v
     cu_q, cu_k = cu_seqlens(lens)
@@ -174,9 +229,11 @@ def make_inputs(lens, heads: int, head_dim: int, seed: int = 0, fp8_pv: bool = F
     inp = Inputs(q=q, k=k, v=v, cu_q=cu_q, cu_k=cu_k)
     if fp8_pv:
         inp.v_e4m3, inp.v_scale = quantize_v_e4m3(v)
+    if fp4_pv:
+        inp.v_e2m1, inp.v_mx_scale = quantize_v_mxfp4(v)
     return inp
 
 
 def workload_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
     return make_inputs(w.doc_lens, w.heads, w.head_dim,
-                       seed=w.seed if seed is None else seed, fp8_pv=w.fp8_pv)
+                       seed=w.seed if seed is None else seed, fp8_pv=w.fp8_pv, fp4_pv=w.fp4_pv)
