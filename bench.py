@@ -22,7 +22,8 @@ Extra objects on the same line:
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
                 the same workload (whole document x head units), in the same unit.
 
-Options: --workload c1|c2|c3|c4|c5 (other workloads, for measurement only),
+Options: --workload c1|c2|c3|c4|c5 (other workloads, for measurement only:
+x_varlen_noncausal_32k, x_causal_fp4pv_32k),
 --variant, --no-cpu-baseline, --counters (a short run for rocprofv3 --pmc: a
 copy kernel of known size, then a few steps), --summarize-counters and
 --summarize-trace (turn rocprofv3 CSV output into the committed summaries).
@@ -40,7 +41,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-MI355X_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # published dense MFMA peaks
+MI355X_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}   # published dense MFMA peaks
 MI355X_HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "head_attention_forward_fmha_amd", "csrc")
 KERNEL_SOURCES = ("fmha_fwd_kernel.hip", "fmha_device.h", "fmha_kernel_params.h")
@@ -63,11 +64,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def pv_format(w) -> int:
+    """The kernels' P.V format template argument: 0 bf16, 1 fp8 e4m3, 2 fp4 e2m1."""
+    return 2 if w.fp4_pv else 1 if w.fp8_pv else 0
+
+
 def kernel_template_name(w, variant):
     if variant == "pipelined":
         return f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}>"
-    return (f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}, "
-            f"{str(w.fp8_pv).lower()}>")
+    return f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}, {pv_format(w)}>"
 
 
 def parse_args():
@@ -78,7 +83,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c4",
-                    choices=sorted(SHORT) + sorted(SHORT.values()) + ["x_varlen_noncausal_32k"])
+                    choices=sorted(SHORT) + sorted(SHORT.values()) +
+                    ["x_varlen_noncausal_32k", "x_causal_fp4pv_32k"])
     ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong", "pipelined"],
                     help="kernel variant (auto picks by problem size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,6 +111,9 @@ def device_inputs(w, dev):
     if w.fp8_pv:
         d["v8"] = inp.v_e4m3.to(dev)
         d["vs"] = inp.v_scale.to(dev)
+    elif w.fp4_pv:
+        d["v4"] = inp.v_e2m1.to(dev)
+        d["vx"] = inp.v_mx_scale.to(dev)
     else:
         d["v"] = inp.v.to(dev)
     d["out"] = torch.empty((w.total_q, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
@@ -118,6 +127,11 @@ def make_step(w, d, variant="auto"):
     if w.fp8_pv:
         def step():
             fm.fwd_fp8pv(d["q"], d["k"], d["v8"], d["vs"], d["cu_q"], d["cu_k"], mq, mk,
+                         causal=w.causal, softmax_scale=w.softmax_scale, out=d["out"],
+                         lse=d["lse"], variant=variant)
+    elif w.fp4_pv:
+        def step():
+            fm.fwd_fp4pv(d["q"], d["k"], d["v4"], d["vx"], d["cu_q"], d["cu_k"], mq, mk,
                          causal=w.causal, softmax_scale=w.softmax_scale, out=d["out"],
                          lse=d["lse"], variant=variant)
     else:
@@ -176,7 +190,12 @@ def cpu_baseline(w, inp, sample_flop):
                    if i.get("user_api") == "blas"] or [1])
     cu_q, cu_k = np.asarray(inp.cu_q), np.asarray(inp.cu_k)
     order = sorted(range(len(cu_q) - 1), key=lambda b: -(cu_q[b + 1] - cu_q[b]))
-    v = oracle.dequantize_v(inp.v_e4m3, inp.v_scale) if w.fp8_pv else inp.v
+    if w.fp8_pv:
+        v = oracle.dequantize_v(inp.v_e4m3, inp.v_scale)
+    elif w.fp4_pv:
+        v = oracle.mx_dequantize_v(inp.v_e2m1, inp.v_mx_scale, w.head_dim)
+    else:
+        v = inp.v
     done, units, parts, dt = 0.0, 0, [], 0.0
     for b in order:
         sq, sk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
@@ -267,8 +286,8 @@ def main():
     if args.summarize_counters:
         # the counters must have been taken on the current sources: the entry is
         # stamped with their hash, and a later change of the kernel voids it
-        from synthetic import WORKLOADS
-        w = WORKLOADS[SHORT.get(args.workload, args.workload)]
+        from synthetic import EXTRA_WORKLOADS, WORKLOADS
+        w = {**WORKLOADS, **EXTRA_WORKLOADS}[SHORT.get(args.workload, args.workload)]
         c = summarize_counters(*args.summarize_counters)
         kernel = c["FETCH_SIZE"]["kernel"]
         variant = ("pingpong" if "pingpong" in kernel else
@@ -318,7 +337,7 @@ def main():
     # one launch per step: the per-step events bracket exactly one kernel
     launch_ms = sum(each) / len(each)
     achieved = flops / (launch_ms * 1e-3) / 1e12
-    dtype = "bf16+fp8" if w.fp8_pv else "bf16"
+    dtype = "bf16+fp8" if w.fp8_pv else "bf16+e2m1" if w.fp4_pv else "bf16"
     peak = MI355X_PEAK_TFLOPS["bf16"]
     variant = (args.variant if args.variant != "auto"
                else fm.auto_variant(w.batch, w.max_seqlen_q, w.heads))
@@ -333,6 +352,11 @@ def main():
         roof["peak_blended_bf16_fp8"] = 1.0 / (0.5 / MI355X_PEAK_TFLOPS["bf16"] +
                                                0.5 / MI355X_PEAK_TFLOPS["fp8"])
         roof["frac_blended"] = round(achieved / roof["peak_blended_bf16_fp8"], 4)
+    if w.fp4_pv:
+        # Q.K^T at the bf16 rate, P.V at the fp4 rate
+        roof["peak_blended_bf16_fp4"] = 1.0 / (0.5 / MI355X_PEAK_TFLOPS["bf16"] +
+                                               0.5 / MI355X_PEAK_TFLOPS["fp4"])
+        roof["frac_blended"] = round(achieved / roof["peak_blended_bf16_fp4"], 4)
     line = {
         "metric": "FMHA fwd TFLOP/s and % of MI355X dense bf16 MFMA peak, d=128, 1 GPU",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -342,7 +366,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.description, "name": w.name, "total_tokens": w.total_q,
                    "docs": w.batch, "heads": w.heads, "head_dim": w.head_dim,
-                   "causal": w.causal, "seed": w.seed, "fp8_pv": w.fp8_pv,
+                   "causal": w.causal, "seed": w.seed, "fp8_pv": w.fp8_pv, "fp4_pv": w.fp4_pv,
                    "kernel_variant": variant},
         "roofline": roof,
         "cpu_baseline": None,

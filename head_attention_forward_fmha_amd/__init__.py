@@ -1,6 +1,6 @@
 """MI355X-native fused multi-head attention forward pass (Python binding).
 
-``fwd`` and ``fwd_fp8pv`` marshal torch tensors into the C ABI of libfmha.so
+``fwd``, ``fwd_fp8pv`` and ``fwd_fp4pv`` marshal torch tensors into the C ABI of libfmha.so
 (include/fmha.h); torch supplies device memory and the current HIP stream, and
 every step of the forward pass runs in the library's gfx950 kernels.
 
@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import FMHA_OK, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8pv", "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
+__all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
            "FmhaError", "EXPORTED_SYMBOLS", "VARIANTS", "load_library"]
 
 
@@ -155,6 +155,44 @@ def fwd_fp8pv(q, k, v_e4m3, v_scale, cu_seqlens_q=None, cu_seqlens_k=None,
                                     ctypes.c_void_p(_stream_handle(dev)))
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_fwd_fp8pv")
+    return out, lse
+
+
+def fwd_fp4pv(q, k, v_e2m1, v_mx_scale, cu_seqlens_q=None, cu_seqlens_k=None,
+              max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+              causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse=None,
+              return_lse: bool = True, variant: str = "auto") -> Tuple:
+    """FMHA forward with P.V in fp4 e2m1 (MXFP4 V, per-group scaled P).
+
+    v_e2m1 uint8 [total_k, h, d/2] (two codes per byte, even d low), v_mx_scale
+    uint8 E8M0 [ceil(total_k/32), h, d]; packed [total, h, d] layout only (dense
+    inputs are the packed layout with batch * seqlen tokens).
+    """
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, 3, dev)
+    _check_tensor("k", k, torch.bfloat16, 3, dev)
+    _check_tensor("v_e2m1", v_e2m1, torch.uint8, 3, dev)
+    _check_tensor("v_mx_scale", v_mx_scale, torch.uint8, 3, dev)
+    s = _prepare(q, k, v_e2m1, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    tk, h, d = k.shape
+    if (tuple(v_e2m1.shape) != (tk, h, d // 2) or q.shape[1:] != k.shape[1:]
+            or tuple(v_mx_scale.shape) != ((tk + 31) // 32, h, d)):
+        raise ValueError("k, v_e2m1, v_mx_scale shapes do not match q")
+    scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    st = lib.fmha_fwd_fp4pv_variant(_ptr(q), _ptr(k), _ptr(v_e2m1), _ptr(v_mx_scale),
+                                    _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"], s["total_q"],
+                                    s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"],
+                                    int(bool(causal)), ctypes.c_float(scale), _ptr(out),
+                                    _ptr(lse), VARIANTS[variant],
+                                    ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_fwd_fp4pv")
     return out, lse
 
 

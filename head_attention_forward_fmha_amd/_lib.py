@@ -25,6 +25,8 @@ EXPORTED_SYMBOLS = (
     "fmha_fwd_fp8pv",
     "fmha_fwd_variant",
     "fmha_fwd_fp8pv_variant",
+    "fmha_fwd_fp4pv",
+    "fmha_fwd_fp4pv_variant",
     "fmha_fwd_auto_variant",
     "fmha_validate_cu_seqlens",
     "fmha_status_string",
@@ -77,6 +79,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmha_fwd_variant.restype = ctypes.c_int
     lib.fmha_fwd_fp8pv_variant.argtypes = _FWD_FP8_ARGS[:-1] + [_i32, _vp]
     lib.fmha_fwd_fp8pv_variant.restype = ctypes.c_int
+    # fp4 P.V: same layout as fp8 (the fourth pointer is the E8M0 exponent array)
+    lib.fmha_fwd_fp4pv.argtypes = _FWD_FP8_ARGS
+    lib.fmha_fwd_fp4pv.restype = ctypes.c_int
+    lib.fmha_fwd_fp4pv_variant.argtypes = _FWD_FP8_ARGS[:-1] + [_i32, _vp]
+    lib.fmha_fwd_fp4pv_variant.restype = ctypes.c_int
     lib.fmha_fwd_auto_variant.argtypes = [_i32, _i32, _i32]
     lib.fmha_fwd_auto_variant.restype = ctypes.c_int32
     lib.fmha_validate_cu_seqlens.argtypes = [_vp, _i32, _i32, _i32]

@@ -17,7 +17,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Checks shared by the bf16 and fp8 P.V entry points. Returns FMHA_OK when the
+// Checks shared by the bf16, fp8 and fp4 P.V entry points. Returns FMHA_OK when the
 // arguments describe a launchable problem.
 fmha_status_t check_common(const void* q, const void* k, const void* v,
                            const int32_t* cu_q, const int32_t* cu_k, int32_t batch,
@@ -141,6 +141,46 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
                              int32_t causal, float softmax_scale,
                              void* out, float* lse, void* stream) {
   return fmha_fwd_fp8pv_variant(q, k, v_e4m3, v_scale, cu_seqlens_q, cu_seqlens_k, batch,
+                                total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads,
+                                head_dim, causal, softmax_scale, out, lse, FMHA_VARIANT_AUTO,
+                                stream);
+}
+
+fmha_status_t fmha_fwd_fp4pv_variant(const void* q, const void* k, const uint8_t* v_e2m1,
+                                     const uint8_t* v_mx_scale,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t total_q, int32_t total_k,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_heads, int32_t head_dim,
+                                     int32_t causal, float softmax_scale,
+                                     void* out, float* lse, int32_t variant, void* stream) {
+  fmha_status_t st = check_common(q, k, v_e2m1, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim,
+                                  causal, softmax_scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (head_dim != 128) return FMHA_ERR_UNSUPPORTED;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PIPELINED) return FMHA_ERR_INVALID_ARG;
+  if (variant == FMHA_VARIANT_PIPELINED) return FMHA_ERR_UNSUPPORTED;
+  if (total_k > 0 && v_mx_scale == nullptr) return FMHA_ERR_INVALID_ARG;
+  if (v_mx_scale && (reinterpret_cast<uintptr_t>(v_mx_scale) & 3u)) return FMHA_ERR_INVALID_ARG;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
+  fmha::FwdParams p = make_params(q, k, v_e2m1, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                                  total_k, max_seqlen_q, max_seqlen_k, num_heads, softmax_scale,
+                                  out, lse);
+  p.v_mx_scale = v_mx_scale;
+  hipError_t e = fmha::launch_fwd_fp4pv(p, head_dim, causal != 0, variant, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+fmha_status_t fmha_fwd_fp4pv(const void* q, const void* k, const uint8_t* v_e2m1,
+                             const uint8_t* v_mx_scale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t total_q, int32_t total_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t num_heads, int32_t head_dim,
+                             int32_t causal, float softmax_scale,
+                             void* out, float* lse, void* stream) {
+  return fmha_fwd_fp4pv_variant(q, k, v_e2m1, v_mx_scale, cu_seqlens_q, cu_seqlens_k, batch,
                                 total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads,
                                 head_dim, causal, softmax_scale, out, lse, FMHA_VARIANT_AUTO,
                                 stream);

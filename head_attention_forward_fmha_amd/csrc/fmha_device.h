@@ -13,8 +13,8 @@
 //   S^T[key, query] = K . Q^T   (v_mfma_f32_32x32x16_bf16, A = K rows from
 //                                LDS, B = Q held in registers)
 //   O^T[d, query]  += V^T . P^T (A = V read from LDS with ds_read_b64_tr_b16,
-//                                or _tr_b8 for e4m3 V; B = P straight from the
-//                                S^T accumulators)
+//                                _tr_b8 for e4m3 V or _tr_b4 for e2m1 V; B = P
+//                                straight from the S^T accumulators)
 // A lane (half = lane/32, column n = lane%32) holds 16 keys of each 32-key S^T
 // block for query n: keys 8*(i/4) + 4*half + i%4 of accumulator register i.
 // The row max and row sum are in-lane reductions plus one v_permlane32_swap
@@ -94,12 +94,17 @@ __device__ __forceinline__ float wave_half_swap_sum(float x) {
 //    spread over all banks.
 // For 256-byte rows (16 chunks) the low two row bits select the high two chunk
 // bits; for 128-byte rows (8 chunks, two rows per bank sweep) row bit 1 selects
-// chunk bit 2 and row bits 2-3 the low two chunk bits. Only the low four row
-// bits matter, so the swizzle repeats every 16 rows.
+// chunk bit 2 and row bits 2-3 the low two chunk bits. For 64-byte rows (e2m1
+// V, 4 chunks, four rows per bank sweep) the transposed reads of a half-wave
+// fetch rows 8a + b (a, b = 0..3) at one chunk: row bits 0-1 already spread
+// them over the sweep, and row bits 3-4 pick the chunk. Only the low five row
+// bits matter, so the swizzle repeats every 32 rows.
 template <int kChunksPerRow>
 __device__ __forceinline__ int swz(int row) {
-  static_assert(kChunksPerRow == 16 || kChunksPerRow == 8, "rows are 128 or 256 bytes");
+  static_assert(kChunksPerRow == 16 || kChunksPerRow == 8 || kChunksPerRow == 4,
+                "rows are 64, 128 or 256 bytes");
   if constexpr (kChunksPerRow == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  if constexpr (kChunksPerRow == 4) return (row >> 3) & 3;
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
@@ -143,6 +148,20 @@ __device__ __forceinline__ void lds_dma_16(uint32_t lds_base, int voffset, i32x4
       : "memory", "scc", "m0");
 }
 
+// HBM -> LDS copy of 4 bytes per active lane from a per-lane address
+// (global_load_lds_dword): lane l writes LDS bytes [lds + 4*l, lds + 4*l + 4).
+// It needs no buffer descriptor in scalar registers; the caller keeps src in
+// bounds. Ordered like lds_dma_16.
+__device__ __forceinline__ void lds_dma_global_4(uint32_t lds_base, const void* src) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off"
+      :
+      : "s"(lds_base), "v"(src)
+      : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const LDS_AS char*)(const char*)p);
@@ -168,9 +187,24 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------- work items
 
+// A (document, head, query block). Keys [k_start, k_start + sk) of the packed
+// tensor are the document's, of which those before k_start + key_lo are
+// hidden (key_lo > 0 only after align_keys_to_blocks).
 struct WorkItem {
-  int head, q_start, k_start, sq, sk, m0;
+  int head, q_start, k_start, sq, sk, m0, key_lo;
 };
+
+// The fp4 P.V path keeps its key tiles on the 32-token blocks of the packed
+// tensor, which carry V's scales and form P's quantisation groups: a document
+// that starts inside a block is widened to the block start, and the extra
+// leading keys are masked. The causal offset sk - sq grows by the same amount,
+// so every query still sees the same keys.
+__device__ __forceinline__ void align_keys_to_blocks(WorkItem& w) {
+  const int r = w.k_start & 31;
+  w.k_start -= r;
+  w.sk += r;
+  w.key_lo = r;
+}
 
 // Work items are the (document, head, query block) triples, ordered
 // (document, head)-major with query blocks inner, longest causal block first,
@@ -247,6 +281,7 @@ __device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int bm,
   w.sq = q_end - w.q_start;
   w.sk = k_end - w.k_start;
   w.m0 = mblock * bm;
+  w.key_lo = 0;
   return w;
 }
 
@@ -274,19 +309,30 @@ __device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f) {
 // ---------------------------------------------------------------- per-wave tile math
 
 // One wave's view of the forward pass: 32 query rows, Q in registers, the
-// running softmax state and the O^T accumulators. kWaves is the workgroup's
-// wave count (it sets how the K/V copies are split among the waves).
-template <int kD, bool kCausal, bool kFp8, int kWaves>
+// running softmax state and the O^T accumulators. kWaves is the number of waves
+// that copy a tile (it sets how the K/V copies are split among them); kPv is
+// the number format of P.V (kPvBf16, kPvE4m3 or kPvE2m1).
+template <int kD, bool kCausal, int kPv, int kWaves>
 struct WaveTile {
+  static constexpr bool kFp8 = kPv == kPvE4m3;
+  static constexpr bool kFp4 = kPv == kPvE2m1;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kRowBytes = kD * 2;               // one K row in bytes
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per K row
   static constexpr int kTileBytes = kBN * kRowBytes;     // one K tile
   static constexpr int kLoadsPerWave = kTileBytes / (kThreads * 16);
-  static constexpr int kVRowBytes = kFp8 ? kD : kD * 2;  // one V row in bytes
+  static constexpr int kVRowBytes = kFp4 ? kD / 2 : (kFp8 ? kD : kD * 2);  // one V row
   static constexpr int kVChunks = kVRowBytes / 16;
   static constexpr int kVTileBytes = kBN * kVRowBytes;
   static constexpr int kVLoadsPerWave = kVTileBytes / (kThreads * 16);
+  // e2m1 V: the tile's E8M0 exponents, [2 blocks of 32 keys][kD], follow its
+  // codes in the same LDS stage; every copying wave fetches all of them (one
+  // 4-byte load per lane), writing identical bytes
+  static constexpr int kVScaleBytes = kFp4 ? 2 * kD : 0;
+  static constexpr int kVStageBytes = kVTileBytes + kVScaleBytes;
+  // vector-memory instructions one wave issues to copy a V tile
+  static constexpr int kVCopyOps = kVLoadsPerWave + (kFp4 ? 1 : 0);
+  static constexpr float kLog2Six = 2.5849625007211562f;   // log2 of e2m1's largest value
   static constexpr int kKSteps = kD / 16;                // QK^T MFMA steps over d
   static constexpr int kDBlocks = kD / 32;               // O^T accumulator blocks
   static constexpr int kKeyBlocks = kBN / 32;            // S^T accumulator blocks
@@ -298,7 +344,9 @@ struct WaveTile {
                 "K tile must split into whole lane loads");
   static_assert(kVLoadsPerWave >= 1 && kVLoadsPerWave * kThreads * 16 == kVTileBytes,
                 "V tile must split into whole lane loads");
-  static_assert(!kFp8 || kBN == 64, "the fp8 P.V step consumes exactly one 64-key tile");
+  static_assert((!kFp8 && !kFp4) || kBN == 64,
+                "the fp8 and fp4 P.V steps consume exactly one 64-key tile");
+  static_assert(!kFp4 || kVScaleBytes == 64 * 4, "the exponent image is one 4-byte load per lane");
 
   // identity
   int lane, col, half, g, gi;
@@ -309,7 +357,11 @@ struct WaveTile {
   f32x16 sacc[kKeyBlocks];
   bf16x8 pb[kBN / 16];   // bf16 P of the last softmaxed tile
   i32x8 pb8;             // e4m3 P of the last softmaxed tile
+  i32x4 pb4;             // e2m1 P of the last softmaxed tile (32 keys per lane)
+  int p_scale;           // its E8M0 group scale for this lane's 32 keys
   float m_run, l_run, c;
+  float m_log2;          // e2m1 path: integer running maximum in exp2 units
+  int key_lo;            // keys before this are hidden (block-aligned fp4 tiles)
   // per-lane LDS byte offsets of the operand reads within a stage's tile
   int k_off[kKSteps];
   int v_off[kVReads][kDBlocks];
@@ -317,6 +369,9 @@ struct WaveTile {
   i32x4 k_rsrc, v_rsrc;
   uint32_t k_stride, v_stride;
   int k_voff[kLoadsPerWave], v_voff[kVLoadsPerWave];
+  const unsigned char* vs_base;  // e2m1 V exponents: (document start block, head), uniform
+  uint32_t vs_stride;
+  int vs_last, vs_lds_delta;      // last block (relative); image offset from lds_v0
 
   __device__ __forceinline__ void init(const FwdParams& p, const WorkItem& w, int wave,
                                        int row_chunk) {
@@ -329,7 +384,9 @@ struct WaveTile {
     qi = wave_q0 + col;
     c = p.scale_log2;
     m_run = -__builtin_inff();
+    m_log2 = -__builtin_inff();
     l_run = 0.f;
+    key_lo = w.key_lo;
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
@@ -351,6 +408,8 @@ struct WaveTile {
     // bf16 V (tr16): rows 16*ks16 + 8r + 4*half + gi/4, d = 32*db + 16*(g&1) + 4*(gi&3).
     // fp8 V (tr8): rows 32*(r>>1) + 16*(r&1) + 8*(e>>2) + 4*half + (e&3), e = gi/2,
     //              byte column 32*db + 16*(g&1) + 8*(gi&1).
+    // fp4 V (tr4): rows 32*half + 8*(gi/4) + 4r + gi%4, byte column 16*db + 8*(g&1)
+    //              (d = 32*db + 16*(g&1) + 0..15).
     // Key block, 16-key step and read index only add multiples of 16 rows,
     // which the swizzle ignores, so they are immediates at the read sites.
 #pragma unroll
@@ -360,7 +419,10 @@ struct WaveTile {
     for (int r = 0; r < kVReads; ++r)
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
-        if constexpr (!kFp8) {
+        if constexpr (kFp4) {
+          const int row = 32 * half + 8 * (gi >> 2) + 4 * r + (gi & 3);
+          v_off[r][db] = row * kVRowBytes + ((db ^ swz<kVChunks>(row)) * 16) + 8 * (g & 1);
+        } else if constexpr (!kFp8) {
           const int row = 8 * r + 4 * half + gi / 4;
           const int d = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
           v_off[r][db] = row * kVRowBytes + (((d / 8) ^ swz<kVChunks>(row)) * 16) + (d % 8) * 2;
@@ -397,13 +459,27 @@ struct WaveTile {
       const int phys = (byte % kVRowBytes) / 16;
       v_voff[r] = row * (int)v_stride + (phys ^ swz<kVChunks>(row)) * 16;
     }
+    // e2m1 V exponents: a tile's two 32-key blocks are rows k_start/32 + 2j and
+    // + 2j + 1 of [blocks, heads, kD]; lane l copies bytes 4l .. 4l + 3 of the
+    // tile's [2][kD] image (block half, d = 4*col .. 4*col + 3). A block past
+    // the end of the array (only in a tile's masked tail, whose V codes read
+    // as zeros) is replaced by the last block, so every read stays in bounds.
+    if constexpr (kFp4) {
+      static_assert(!kFp4 || kD == 128, "the exponent image is [2][128]");
+      vs_stride = (uint32_t)p.heads * kD;
+      const int blk0 = w.k_start / 32;
+      const int n_blocks = (p.total_k + 31) / 32;
+      vs_base = p.v_mx_scale + (size_t)blk0 * vs_stride + (size_t)w.head * kD;
+      vs_last = max(n_blocks - 1 - blk0, 0);
+      vs_lds_delta = kVTileBytes - 1024 * wave;
+    }
   }
 
   // Byte offset of a tile in the copy descriptors' buffers. It is uniform; the
-  // persistent (causal) kernels say so explicitly, which keeps it in a scalar
-  // register there (the buffer loads take it only from one).
+  // persistent (causal) kernels and the fp4 ones say so explicitly, which keeps
+  // it in a scalar register there (the buffer loads take it only from one).
   __device__ __forceinline__ static int scalar_offset(int off) {
-    if constexpr (kCausal) return __builtin_amdgcn_readfirstlane(off);
+    if constexpr (kCausal || kFp4) return __builtin_amdgcn_readfirstlane(off);
     return off;
   }
 
@@ -418,6 +494,15 @@ struct WaveTile {
     }
     k_stride = __builtin_amdgcn_readfirstlane(k_stride);
     v_stride = __builtin_amdgcn_readfirstlane(v_stride);
+    if constexpr (kFp4) {
+      const uint64_t b = reinterpret_cast<uint64_t>(vs_base);
+      vs_base = reinterpret_cast<const unsigned char*>(
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b));
+      vs_stride = __builtin_amdgcn_readfirstlane(vs_stride);
+      vs_last = __builtin_amdgcn_readfirstlane(vs_last);
+      key_lo = __builtin_amdgcn_readfirstlane(key_lo);
+    }
   }
 
   // This wave's share of the copy of K tile j into K stage kStage (lds_k0 is
@@ -431,9 +516,17 @@ struct WaveTile {
   }
   template <int kStage, int kR>
   __device__ __forceinline__ void copy_v_one(int j, uint32_t lds_v0) {
-    lds_dma_16<kStage * kVTileBytes + 1024 * kWaves * kR>(
+    lds_dma_16<kStage * kVStageBytes + 1024 * kWaves * kR>(
         lds_v0, v_voff[kR], v_rsrc,
         scalar_offset((int)((uint32_t)(j * kBN) * v_stride)));
+  }
+  // e2m1 V: tile j's exponent image (the same 256 bytes from every wave)
+  template <int kStage>
+  __device__ __forceinline__ void copy_v_scales(int j, uint32_t lds_v0) {
+    const uint32_t base =
+        __builtin_amdgcn_readfirstlane(lds_v0 + vs_lds_delta + kStage * kVStageBytes);
+    const int rb = min(2 * j + half, vs_last);
+    lds_dma_global_4(base, vs_base + (size_t)(uint32_t)rb * vs_stride + 4 * col);
   }
   template <int kStage>
   __device__ __forceinline__ void copy_k(int j, uint32_t lds_k0) {
@@ -446,6 +539,7 @@ struct WaveTile {
     [&]<int... kR>(std::integer_sequence<int, kR...>) {
       (copy_v_one<kStage, kR>(j, lds_v0), ...);
     }(std::make_integer_sequence<int, kVLoadsPerWave>());
+    if constexpr (kFp4) copy_v_scales<kStage>(j, lds_v0);
   }
 
   // Does any of this wave's rows see a key of tile j?
@@ -495,25 +589,119 @@ struct WaveTile {
   }
 
   // Causal mask (key j visible to query i iff j <= i + sk - sq) and key tail
-  // (j < sk), on tiles that need it; then the online softmax and P.
+  // (j < sk), on tiles that need it; the fp4 path also hides keys before key_lo
+  // (block alignment). Then the online softmax and P.
   __device__ __forceinline__ void softmax(int j, int sk, int causal_off) {
     const int kt0 = j * kBN;
-    const bool need_mask = (kt0 + kBN > sk) || (kCausal && (kt0 + kBN - 1 > wave_q0 + causal_off));
+    bool need_mask = (kt0 + kBN > sk) || (kCausal && (kt0 + kBN - 1 > wave_q0 + causal_off));
+    if constexpr (kFp4) need_mask = need_mask || (kt0 < key_lo);
     if (need_mask) {
       const int lim = kCausal ? min(sk - 1, qi + causal_off) : sk - 1;
+      if constexpr (kFp4) {
+        // visible iff key_lo <= key <= lim, as one unsigned compare per key
+        const uint32_t n_vis = (uint32_t)max(lim - key_lo + 1, 0);
+        const int base = kt0 + 4 * half - key_lo;
 #pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt0 + 32 * kb + (i / 4) * 8 + 4 * half + (i % 4);
-          if (key > lim) sacc[kb][i] = -__builtin_inff();
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int rel = base + 32 * kb + (i / 4) * 8 + (i % 4);
+            if ((uint32_t)rel >= n_vis) sacc[kb][i] = -__builtin_inff();
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt0 + 32 * kb + (i / 4) * 8 + 4 * half + (i % 4);
+            if (key > lim) sacc[kb][i] = -__builtin_inff();
+          }
+      }
     }
-    if constexpr (!kFp8) {
+    if constexpr (kFp4) {
+      softmax_fp4();
+    } else if constexpr (!kFp8) {
       softmax_lazy();
     } else {
       softmax_exact();
     }
+  }
+
+  // e2m1 P with per-group scales (log-domain quantisation). A lane holds 16
+  // keys of each 32-key half of the tile (accumulator kb = key block kb); the
+  // keys of one query row in one 32-key block form a quantisation group. exp2
+  // is monotonic, so a group's largest p comes from its largest score g, and
+  // its power-of-two scale 2^E, E = ceil(c*g - log2 6), keeps every p/2^E <= 6
+  // (e2m1's largest value). The division by 2^E is a subtraction inside the
+  // exp2 argument: p_hat = exp2(fma(s, c, -E)), one multiply-add per score.
+  //
+  // The running maximum is an integer M in exp2 units (m_log2), raised only
+  // when a tile's p would exceed 2^8, so every O and l rescale is an exact
+  // power of two and the quantised P does not depend on M: the codes are a
+  // function of the scores alone. E - M (at most 6) is the group's E8M0 scale
+  // byte - 127 for the P.V MFMA; the row sum adds the fp32 p_hat * 2^(E - M),
+  // the values before rounding.
+  __device__ __forceinline__ void softmax_fp4() {
+    float ga[kKeyBlocks];
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb) {
+      float mp[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], sacc[kb][i]);
+      ga[kb] = wave_half_swap_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+    }
+    const float cmx = fmaxf(ga[0], ga[1]) * c;
+    // -inf + 8 = -inf: a first finite maximum always raises, an empty row never
+    const bool raise = cmx > m_log2 + 8.f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? __builtin_ceilf(cmx) : m_log2;
+      // 2^(M_old - M_new): 1 for rows not raised, 0 for a first maximum (the
+      // clamp also absorbs -inf and the NaN of -inf - -inf, where O = l = 0)
+      const float alpha = __builtin_ldexpf(1.f, (int)fmaxf(m_log2 - m_new, -200.f));
+      m_log2 = m_new;
+      rescale(alpha);
+    }
+    const float m_safe = (m_log2 == -__builtin_inff()) ? 0.f : m_log2;
+    float rel[kKeyBlocks], add[kKeyBlocks];
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb) {
+      // an empty group (g = -inf) takes the smallest scale; its p are zero
+      const float e = __builtin_ceilf(__builtin_fmaf(ga[kb], c, -kLog2Six));
+      rel[kb] = fmaxf(e - m_safe, -127.f);
+      add[kb] = -(m_safe + rel[kb]);
+    }
+    // Packing. Key 32*kb + 8a + 4*half + b (a, b = 0..3) of this lane is
+    // rounded into nibble (b) of the 16-bit field a%2 of word[kb][a/2]. One
+    // v_permlane32_swap per word pair then leaves lane n (half 0) with the
+    // block-0 words of both halves and lane n+32 with the block-1 words, so
+    // operand nibble k of a lane is key 32*half + pi(k), with
+    // pi = 0-3, 8-11 | 16-19, 24-27 | 4-7, 12-15 | 20-23, 28-31 (words 0..3);
+    // the transposed V reads fetch keys in the same order.
+    uint32_t word[kKeyBlocks][2] = {{0u, 0u}, {0u, 0u}};
+    float rs[kKeyBlocks][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    static_for<kKeyBlocks * 8>([&](auto n_tag) {
+      constexpr int n = decltype(n_tag)::value;
+      constexpr int kb = n / 8, a = (n % 8) / 2, bb = n % 2;
+      constexpr int i0 = 4 * a + 2 * bb;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0], c, add[kb]));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 1], c, add[kb]));
+      rs[kb][bb] += p0 + p1;
+      word[kb][a / 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word[kb][a / 2], p0, p1, 1.f,
+                                                                 2 * (a % 2) + bb);
+    });
+    l_run += __builtin_ldexpf(rs[0][0] + rs[0][1], (int)rel[0]) +
+             __builtin_ldexpf(rs[1][0] + rs[1][1], (int)rel[1]);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane32_swap((int)word[0][w], (int)word[1][w], false, false);
+      pb4[w] = r[0];
+      pb4[2 + w] = r[1];
+    }
+    // lane n takes group 0's exponent, lane n+32 group 1's (both lanes hold both)
+    const auto rs_sel = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, rel[0]),
+                                                         __builtin_bit_cast(int, rel[1]), false,
+                                                         false);
+    p_scale = (int)__builtin_bit_cast(float, rs_sel[0]) + 127;
   }
 
   // bf16 P: lazy maximum. The maximum in use (m_run) is kept as long as every
@@ -628,7 +816,22 @@ struct WaveTile {
 
   // O^T += V^T P^T for the tile at vs (LDS, generic pointer).
   __device__ __forceinline__ void pv(const char* vs) {
-    if constexpr (!kFp8) {
+    if constexpr (kFp4) {
+      // all 64 keys of the tile in one e2m1 MFMA per d block; lane (half, m)
+      // supplies d row 32*db + m and keys 32*half + pi(0..31), and scales them
+      // by the exponent of key block half, column d
+      const unsigned char* vsc = (const unsigned char*)(vs + kVTileBytes) + half * kD + col;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db) {
+        const auto lo = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + v_off[0][db]));
+        const auto hi = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + v_off[1][db]));
+        const int sa = vsc[32 * db];
+        const i32x8 a = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
+        const i32x8 b = {pb4[0], pb4[1], pb4[2], pb4[3], 0, 0, 0, 0};
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, oacc[db], 4, 4, 0, sa,
+                                                                   0, p_scale);
+      }
+    } else if constexpr (!kFp8) {
       // 16 keys per MFMA. Lane (half, m) needs V[keys 16*ks16 + 8r + 4*half
       // + 0..3][d = 32*db + m]; source lane gi of group g reads 4 d-values of
       // key row (.. + gi/4). The A operands of MFMA i + kAhead are read while
@@ -851,6 +1054,7 @@ struct WaveTile {
     l_run = wave_half_swap_sum(l_run);
     if (qi >= w.sq) return;
     // fp8: O = v_scale * sum(P_hat V_codes) / l, where l carries the same 2^kPScaleLog2
+    // (fp4: the block and group scales are applied inside the MFMA)
     const float num_scale = kFp8 ? p.v_scale[w.head] : 1.f;
     const float inv_l = (l_run > 0.f) ? num_scale / l_run : 0.f;
     const int row_stride = p.heads * kD;
@@ -868,8 +1072,9 @@ struct WaveTile {
     if (p.lse != nullptr && half == 0) {
       float lse = -__builtin_inff();
       const float lsub = kFp8 ? kPScaleLog2 : 0.f;
+      const float mlog2 = kFp4 ? m_log2 : m_run * c;
       if (l_run > 0.f)
-        lse = (m_run * c + (__builtin_amdgcn_logf(l_run) - lsub)) * 0.69314718055994531f;
+        lse = (mlog2 + (__builtin_amdgcn_logf(l_run) - lsub)) * 0.69314718055994531f;
       p.lse[(size_t)w.head * p.total_q + w.q_start + qi] = lse;
     }
   }

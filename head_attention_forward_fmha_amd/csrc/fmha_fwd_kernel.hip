@@ -36,17 +36,18 @@ constexpr int kWaves4 = 4;
 constexpr int kBM4 = kWaves4 * 32;  // query rows per workgroup
 static_assert(kBM4 == kRowsFourWave, "4-wave block height");
 
-template <int kD, bool kCausal, bool kFp8>
+template <int kD, bool kCausal, int kPv>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves4 * 64, kWaves4 * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fmha_fwd_kernel(FwdParams params) {
-  using WT = WaveTile<kD, kCausal, kFp8, kWaves4>;
+  using WT = WaveTile<kD, kCausal, kPv, kWaves4>;
   __shared__ __attribute__((aligned(1024))) char smem_k[2][WT::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char smem_v[2][WT::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_v[2][WT::kVStageBytes];
 
   auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
-  const WorkItem w = decode_work_item(p, kBM4, item);
+  WorkItem w = decode_work_item(p, kBM4, item);
   if (w.m0 >= w.sq) return;  // uniform over the workgroup
+  if constexpr (WT::kFp4) align_keys_to_blocks(w);
   const int causal_off = w.sk - w.sq;
   int kend = w.sk;
   if (kCausal) kend = min(w.sk, max(0, w.m0 + kBM4 + causal_off));
@@ -65,7 +66,7 @@ void fmha_fwd_kernel(FwdParams params) {
     if (j + 1 < n_tiles) {
       t.template copy_k<stage ^ 1>(j + 1, k_lds0);
       t.template copy_v<stage ^ 1>(j + 1, v_lds0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave + WT::kVLoadsPerWave));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave + WT::kVCopyOps));
     } else {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
@@ -111,19 +112,20 @@ struct NoPhaseTrace {
   __device__ __forceinline__ void mark(int /*event*/) {}
 };
 
-template <int kD, bool kCausal, bool kFp8, typename Trace = NoPhaseTrace>
+template <int kD, bool kCausal, int kPv, typename Trace = NoPhaseTrace>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves8 * 64, kWaves8 * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fmha_fwd_pingpong_kernel(FwdParams params) {
   // each group of 4 waves copies whole tiles, so the tile math is set up for 4
   // copying waves
-  using WT = WaveTile<kD, kCausal, kFp8, 4>;
+  using WT = WaveTile<kD, kCausal, kPv, 4>;
   __shared__ __attribute__((aligned(1024))) char smem_k[kStages8][WT::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char smem_v[kStages8][WT::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_v[kStages8][WT::kVStageBytes];
 
   auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
-  const WorkItem w = decode_work_item(p, kBM8, item);
+  WorkItem w = decode_work_item(p, kBM8, item);
   if (w.m0 >= w.sq) return;  // uniform over the workgroup
+  if constexpr (WT::kFp4) align_keys_to_blocks(w);
   const int causal_off = w.sk - w.sq;
   int kend = w.sk;
   if (kCausal) kend = min(w.sk, max(0, w.m0 + kBM8 + causal_off));
@@ -134,7 +136,7 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   // 32-row chunks alternate between the groups, which evens out the causal work
   WT t;
   t.init(p, w, wave & 3, 2 * (wave & 3) + grp);
-  if constexpr (kCausal) t.pin_copy_state();
+  if constexpr (kCausal || WT::kFp4) t.pin_copy_state();
   const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * (wave & 3)]);
   const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * (wave & 3)]);
   Trace trace;
@@ -190,7 +192,7 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
       valu_phase(j);
       trace.mark(4);
       // the copies of V tile j (issued in slot 2j-1) have landed
-      if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kVLoadsPerWave));
+      if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kVCopyOps));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     } else {
       mfma_phase(j, r_tag);
@@ -239,7 +241,7 @@ template <int kD, bool kCausal>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWavesPipe * 64, kWavesPipe * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fmha_fwd_pipe_kernel(FwdParams params) {
-  using WT = WaveTile<kD, kCausal, false, kWavesPipe>;
+  using WT = WaveTile<kD, kCausal, kPvBf16, kWavesPipe>;
   __shared__ __attribute__((aligned(1024))) char smem_k[2][WT::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char smem_v[2][WT::kVTileBytes];
 
@@ -358,10 +360,10 @@ static int device_cus() {
   return cus;
 }
 
-template <int kD, bool kCausal, bool kFp8>
+template <int kD, bool kCausal, int kPv>
 static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   FwdParams q = p;
-  const int variant_run = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads, kFp8);
+  const int variant_run = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads);
   const bool use8 = variant_run == kVariantPingPong;
   const int bm = use8 ? kBM8 : kBM4;
   q.n_mblocks = (p.max_seqlen_q + bm - 1) / bm;
@@ -375,16 +377,16 @@ static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   const long long grid =
       kCausal ? (std::min(n_items, resident) + kXcds - 1) / kXcds * kXcds : n_items;
   if (variant_run == kVariantPipelined) {
-    if constexpr (!kFp8)
+    if constexpr (kPv == kPvBf16)
       hipLaunchKernelGGL((fmha_fwd_pipe_kernel<kD, kCausal>), dim3((unsigned)grid),
                          dim3(kWavesPipe * 64), 0, stream, q);
     else
       return hipErrorInvalidValue;
   } else if (use8)
-    hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<kD, kCausal, kFp8>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<kD, kCausal, kPv>), dim3((unsigned)grid),
                        dim3(kWaves8 * 64), 0, stream, q);
   else
-    hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kFp8>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kPv>), dim3((unsigned)grid),
                        dim3(kWaves4 * 64), 0, stream, q);
   return hipGetLastError();
 }
@@ -392,17 +394,24 @@ static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, int variant,
                            hipStream_t stream) {
   if (head_dim == 128)
-    return causal ? launch<128, true, false>(p, variant, stream)
-                  : launch<128, false, false>(p, variant, stream);
-  return causal ? launch<64, true, false>(p, variant, stream)
-                : launch<64, false, false>(p, variant, stream);
+    return causal ? launch<128, true, kPvBf16>(p, variant, stream)
+                  : launch<128, false, kPvBf16>(p, variant, stream);
+  return causal ? launch<64, true, kPvBf16>(p, variant, stream)
+                : launch<64, false, kPvBf16>(p, variant, stream);
 }
 
 hipError_t launch_fwd_fp8pv(const FwdParams& p, int head_dim, bool causal, int variant,
                             hipStream_t stream) {
   if (head_dim != 128) return hipErrorInvalidValue;
-  return causal ? launch<128, true, true>(p, variant, stream)
-                : launch<128, false, true>(p, variant, stream);
+  return causal ? launch<128, true, kPvE4m3>(p, variant, stream)
+                : launch<128, false, kPvE4m3>(p, variant, stream);
+}
+
+hipError_t launch_fwd_fp4pv(const FwdParams& p, int head_dim, bool causal, int variant,
+                            hipStream_t stream) {
+  if (head_dim != 128) return hipErrorInvalidValue;
+  return causal ? launch<128, true, kPvE2m1>(p, variant, stream)
+                : launch<128, false, kPvE2m1>(p, variant, stream);
 }
 
 }  // namespace fmha

@@ -14,6 +14,7 @@ struct FwdParams {
   const int32_t* cu_q;    // [batch + 1] or nullptr (dense)
   const int32_t* cu_k;    // [batch + 1] or nullptr (dense)
   const float* v_scale;   // [heads] (fp8 P.V only)
+  const uint8_t* v_mx_scale;  // E8M0 [ceil(total_k / 32), heads, d] (fp4 P.V only)
   void* out;              // bf16 [total_q, heads, d]
   float* lse;             // fp32 [heads, total_q] or nullptr
   int32_t batch;
@@ -25,6 +26,12 @@ struct FwdParams {
   float scale_log2;       // softmax_scale * log2(e)
   int32_t n_mblocks;      // query blocks per document (set by the launcher)
 };
+
+// Number formats of the P.V product: bf16, fp8 e4m3 (one fp32 scale per head
+// for V) or fp4 e2m1 (MXFP4 V, per-group power-of-two scales for P).
+constexpr int kPvBf16 = 0;
+constexpr int kPvE4m3 = 1;
+constexpr int kPvE2m1 = 2;
 
 // Kernel variants (the values of fmha.h's FMHA_VARIANT_*).
 constexpr int kVariantAuto = 0;      // pick by problem size
@@ -41,9 +48,7 @@ constexpr int kRowsPipelined = 128;
 // problem has at least 128 blocks of 256 query rows (half the CUs of an
 // MI355X), else the 4-wave kernel, whose smaller blocks spread a small problem
 // over more CUs.
-inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int32_t heads,
-                           bool fp8 = false) {
-  (void)fp8;
+inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int32_t heads) {
   if (variant != kVariantAuto) return variant;
   const long long blocks = ((long long)max_seqlen_q + kRowsPingPong - 1) / kRowsPingPong *
                            heads * batch;
@@ -53,6 +58,8 @@ inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, bool causal, int variant,
                            hipStream_t stream);
 hipError_t launch_fwd_fp8pv(const FwdParams& p, int head_dim, bool causal, int variant,
+                            hipStream_t stream);
+hipError_t launch_fwd_fp4pv(const FwdParams& p, int head_dim, bool causal, int variant,
                             hipStream_t stream);
 
 }  // namespace fmha

@@ -108,8 +108,41 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
                              void* out, float* lse, void* stream);
 
 /*
+ * Forward pass with P.V in fp4 (OCP e2m1 with power-of-two block scales), the
+ * FP4 PV variant of "Kernel Bottleneck Tuning (validated on FA4 FP4/FP8 PV,
+ * GB300)" (introduction; section 4, log-domain refactoring). Q.K^T stays bf16.
+ *
+ * V arrives in OCP MXFP4 along the token axis of the packed tensor:
+ *   v_e2m1      uint8 [total_k, num_heads, head_dim / 2], 16-byte aligned: two
+ *               e2m1 codes per byte, even d in the low nibble;
+ *   v_mx_scale  uint8 [ceil(total_k / 32), num_heads, head_dim], 4-byte
+ *               aligned: E8M0 exponents, one per 32 consecutive tokens (from
+ *               token 0 of the packed tensor), head and d;
+ *   V[t, h, d] = e2m1(code[t, h, d]) * 2^(v_mx_scale[t / 32, h, d] - 127).
+ * A 32-token block may span two documents; documents may start anywhere.
+ *
+ * P is quantised per group, a group being the keys of one query row inside one
+ * 32-token block: with c = softmax_scale * log2(e) and g the group's largest
+ * raw score q.k, E = ceil(c*g - log2 6) and P_hat = 2^E * e2m1(2^(c*q.k - E))
+ * (round to nearest even), the division by 2^E being a subtraction inside the
+ * exp2 argument. The quantised P depends only on the scores (not on the order
+ * in which key tiles are visited). The row sum uses the values before rounding,
+ * so LSE is that of the exact scores, and O = sum P_hat V / sum 2^(c q.k).
+ * Every other argument as for fmha_fwd; head_dim must be 128; v_mx_scale may be
+ * NULL only when total_k == 0.
+ */
+fmha_status_t fmha_fwd_fp4pv(const void* q, const void* k, const uint8_t* v_e2m1,
+                             const uint8_t* v_mx_scale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t total_q, int32_t total_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t num_heads, int32_t head_dim,
+                             int32_t causal, float softmax_scale,
+                             void* out, float* lse, void* stream);
+
+/*
  * Kernel variant selection, for testing and tuning. FMHA_VARIANT_AUTO (what
- * fmha_fwd and fmha_fwd_fp8pv use) takes the 8-wave ping-pong kernel when the
+ * fmha_fwd, fmha_fwd_fp8pv and fmha_fwd_fp4pv use) takes the 8-wave ping-pong kernel when the
  * problem has at least 128 blocks of 256 query rows, else the 4-wave kernel.
  * All variants compute the same function. They currently run the same per-row
  * arithmetic in the same key-tile order and give bit-identical results; the ABI
@@ -119,7 +152,7 @@ fmha_status_t fmha_fwd_fp8pv(const void* q, const void* k, const uint8_t* v_e4m3
 #define FMHA_VARIANT_FOUR_WAVE 1   /* 4 waves, 128 query rows per workgroup   */
 #define FMHA_VARIANT_PINGPONG 2    /* 8 waves in two phase-shifted groups     */
 #define FMHA_VARIANT_PIPELINED 3   /* 4 waves, each software-pipelined; bf16
-                                      only (fp8 P.V: FMHA_ERR_UNSUPPORTED)   */
+                                      only (fp8/fp4 P.V: FMHA_ERR_UNSUPPORTED) */
 
 /* fmha_fwd with an explicit kernel variant (any other value: INVALID_ARG). */
 fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,
@@ -133,6 +166,17 @@ fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,
 /* fmha_fwd_fp8pv with an explicit kernel variant (any other value: INVALID_ARG). */
 fmha_status_t fmha_fwd_fp8pv_variant(const void* q, const void* k, const uint8_t* v_e4m3,
                                      const float* v_scale,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t total_q, int32_t total_k,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_heads, int32_t head_dim,
+                                     int32_t causal, float softmax_scale,
+                                     void* out, float* lse, int32_t variant, void* stream);
+
+/* fmha_fwd_fp4pv with an explicit kernel variant (any other value: INVALID_ARG;
+ * FMHA_VARIANT_PIPELINED: FMHA_ERR_UNSUPPORTED). */
+fmha_status_t fmha_fwd_fp4pv_variant(const void* q, const void* k, const uint8_t* v_e2m1,
+                                     const uint8_t* v_mx_scale,
                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                      int32_t batch, int32_t total_q, int32_t total_k,
                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -162,7 +206,7 @@ const char* fmha_status_string(fmha_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int32_t fmha_abi_version(void);
 
-#define FMHA_ABI_VERSION ((1 << 16) | 0)
+#define FMHA_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

@@ -34,10 +34,12 @@ Two answers are computed:
     inputs define; the P quantisation is the method's approximation, bounded
     by ``FP4Emulation.bound``.
   * ``attention_fp4pv_emulated``: the method's quantised result, computed from
-    the definition above in fp64, plus what makes it unique or ambiguous:
-    elements whose scaled value lies within a relative 1e-4 of an e2m1 rounding
-    midpoint, and groups whose E_G argument lies within 1e-4 of an integer,
-    either of which fp32 scores may push to the other side.
+    the definition above in fp64, plus what is left ambiguous when the scores
+    are fp32 (as on the GPU): elements whose scaled value lies within a
+    relative 1e-4 of an e2m1 rounding midpoint may round either way, and a
+    group whose E_G argument lies within 1e-4 of an integer may take the
+    neighbouring exponent. Either choice is a correct result of the method; the
+    ``ambiguity`` term bounds how far the alternatives move O.
 """
 
 from __future__ import annotations
@@ -54,15 +56,21 @@ LOG2_6 = float(np.log2(6.0))
 AMBIGUOUS_REL = 1e-4          # see the module docstring
 
 
+def _e2m1_value(c: int) -> float:
+    """Value of one 4-bit e2m1 code, from the format definition."""
+    sign = -1.0 if c & 0x8 else 1.0
+    e, m = (c >> 1) & 0x3, c & 0x1
+    if e == 0:
+        return sign * m / 2.0                       # subnormal
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+_E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
 def e2m1_decode(codes) -> np.ndarray:
     """Decode 4-bit e2m1 codes (low nibble of each integer) to float64."""
-    c = np.asarray(codes).astype(np.int64) & 0xF
-    sign = np.where(c & 0x8, -1.0, 1.0)
-    e = (c >> 1) & 0x3
-    m = (c & 0x1).astype(np.float64)
-    normal = (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
-    sub = m / 2.0
-    return sign * np.where(e == 0, sub, normal)
+    return _E2M1_TABLE[np.asarray(codes).astype(np.intp) & 0xF]
 
 
 _POS_CODES = np.arange(8, dtype=np.int64)
@@ -123,8 +131,8 @@ def mx_dequantize_v(v_packed, v_scales, head_dim: int) -> np.ndarray:
     sc = v_scales.numpy() if hasattr(v_scales, "numpy") else np.asarray(v_scales)
     t = codes.shape[0]
     blk = np.arange(t) // MX_BLOCK
-    exps = sc.astype(np.float64)[blk] - 127.0
-    return e2m1_decode(codes) * np.exp2(exps)
+    exps = sc.astype(np.int64)[blk] - 127
+    return np.ldexp(e2m1_decode(codes), exps)
 
 
 def attention_fp4pv(q, k, v_packed, v_scales, cu_seqlens_q, cu_seqlens_k, causal: bool,
@@ -149,9 +157,10 @@ def fp32_log2e_scale(softmax_scale: float) -> float:
 def group_exponents(raw_gmax: np.ndarray, c: float):
     """E_G = ceil(c g - log2 6) from fp32 group maxima, decided in fp32.
 
-    Returns (E as float64 with -inf for empty groups, distance of the argument
-    to the nearest integer). The argument is formed from the fp32 score
-    maximum with one rounding to fp32, as a fused multiply-add computes it.
+    Returns (E as float64 with -inf for empty groups, frac = arg - floor(arg)
+    of the argument, NaN for empty groups). The argument is formed from the
+    fp32 score maximum with one rounding to fp32, as a fused multiply-add
+    computes it.
     """
     g32 = raw_gmax.astype(np.float32).astype(np.float64)
     with np.errstate(invalid="ignore"):
@@ -159,8 +168,8 @@ def group_exponents(raw_gmax: np.ndarray, c: float):
     arg = arg.astype(np.float64)
     e = np.ceil(arg)
     with np.errstate(invalid="ignore"):
-        dist = np.where(np.isfinite(arg), np.abs(arg - np.round(arg)), np.inf)
-    return e, dist
+        frac = np.where(np.isfinite(arg), arg - np.floor(arg), np.nan)
+    return e, frac
 
 
 def quantize_p_row_block(raw: np.ndarray, key_tokens: np.ndarray, c: float):
@@ -169,19 +178,20 @@ def quantize_p_row_block(raw: np.ndarray, key_tokens: np.ndarray, c: float):
     raw [r, sk] fp64 raw scores q.k of one (document, head); key_tokens [sk]
     the packed token index of each key (groups are the 32-token blocks).
     Returns (x [r, sk] = 2^(c r - E_G) before rounding, codes, E [r, sk]
-    (each key's group exponent), group-ambiguity distance per key).
+    (each key's group exponent), and the fractional part arg - floor(arg) of
+    each key's group exponent argument).
     """
     blk = np.asarray(key_tokens) // MX_BLOCK
     starts = np.flatnonzero(np.r_[True, blk[1:] != blk[:-1]]) if blk.size else np.zeros(0, int)
     counts = np.diff(np.r_[starts, blk.size])
     gmax = np.maximum.reduceat(raw, starts, axis=1) if blk.size else np.zeros((raw.shape[0], 0))
-    e_g, dist_g = group_exponents(gmax, c)
+    e_g, frac_g = group_exponents(gmax, c)
     e = np.repeat(e_g, counts, axis=1)
-    dist = np.repeat(dist_g, counts, axis=1)
+    frac = np.repeat(frac_g, counts, axis=1)
     finite = np.isfinite(raw)
     with np.errstate(invalid="ignore", over="ignore"):
         x = np.where(finite, np.exp2(np.where(finite, c * raw - e, -np.inf)), 0.0)
-    return x, e2m1_encode(x), e, dist
+    return x, e2m1_encode(x), e, frac
 
 
 @dataclass
@@ -189,8 +199,8 @@ class FP4Emulation:
     out: np.ndarray        # [n, dv] emulated O
     lse: np.ndarray        # [n] LSE of the unquantised scores
     bound: np.ndarray      # [n, dv] bound on |O_emulated - O_exact|
-    ambiguity: np.ndarray  # [n, dv] what element rounding flips can change O by
-    group_tie: np.ndarray  # [n] bool: some group exponent is a near tie
+    ambiguity: np.ndarray  # [n, dv] how far the ambiguous roundings can move O
+    group_tie: np.ndarray  # [n] bool: some group exponent is a near tie (counted in ambiguity)
 
 
 def _fp4_rows(raw: np.ndarray, key_tokens: np.ndarray, vh: np.ndarray, c: float):
@@ -199,7 +209,7 @@ def _fp4_rows(raw: np.ndarray, key_tokens: np.ndarray, vh: np.ndarray, c: float)
     if raw.shape[1] == 0:      # a document without keys: O = 0, LSE = -inf
         z = np.zeros((r, dv))
         return z, np.full(r, -np.inf), z.copy(), z.copy(), np.zeros(r, dtype=bool)
-    x, codes, e, dist = quantize_p_row_block(raw, key_tokens, c)
+    x, codes, e, frac = quantize_p_row_block(raw, key_tokens, c)
     finite = np.isfinite(raw)
     any_vis = finite.any(axis=1)
     with np.errstate(invalid="ignore"):
@@ -216,8 +226,22 @@ def _fp4_rows(raw: np.ndarray, key_tokens: np.ndarray, vh: np.ndarray, c: float)
     err = rel * np.maximum(0.25, x / 4.0)
     bound = (err @ np.abs(vh)) * inv_l[:, None]
     amb = np.where(_e2m1_midpoint_distance(x) < AMBIGUOUS_REL, rel * _e2m1_step(x), 0.0)
+    # a group whose exponent argument sits next to an integer may take the
+    # neighbouring exponent (E - 1 just above the integer, E + 1 just below):
+    # its keys' P_hat then follow the other grid
+    with np.errstate(invalid="ignore"):
+        below = finite & (frac < AMBIGUOUS_REL)            # ceil may have been one lower
+        above = finite & (frac > 1.0 - AMBIGUOUS_REL)      # ceil may have been one higher
+    tie = below | above
+    if tie.any():
+        e_alt = np.where(below, e - 1.0, e + 1.0)
+        with np.errstate(invalid="ignore", over="ignore"):
+            x_alt = np.where(tie, np.exp2(np.where(tie, c * raw - e_alt, -np.inf)), 0.0)
+            rel_alt = np.where(tie, np.exp2(np.where(tie, e_alt, 0.0) - m[:, None]), 0.0)
+        p_alt = e2m1_decode(e2m1_encode(x_alt)) * rel_alt
+        amb = amb + np.where(tie, np.abs(p_alt - p_hat), 0.0)
     ambiguity = (amb @ np.abs(vh)) * inv_l[:, None]
-    group_tie = (np.where(finite, dist, np.inf) < AMBIGUOUS_REL).any(axis=1)
+    group_tie = tie.any(axis=1)
     with np.errstate(divide="ignore"):
         lse = np.where(any_vis, (m + np.log2(np.where(any_vis, l, 1.0))) * np.log(2.0), -np.inf)
     return out, lse, bound, ambiguity, group_tie

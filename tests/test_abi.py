@@ -24,8 +24,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["fmha_fwd", "fmha_fwd_fp8pv", "fmha_fwd_variant",
-                            "fmha_fwd_fp8pv_variant", "fmha_fwd_auto_variant",
-                            "fmha_validate_cu_seqlens",
+                            "fmha_fwd_fp8pv_variant", "fmha_fwd_fp4pv", "fmha_fwd_fp4pv_variant",
+                            "fmha_fwd_auto_variant", "fmha_validate_cu_seqlens",
                             "fmha_status_string", "fmha_abi_version"])
 
 
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert set(fm.EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert fm.abi_version() == (1 << 16)
+    assert fm.abi_version() == (1 << 16) | 1
 
 
 def test_status_strings():
@@ -132,6 +132,31 @@ def test_fp8_rejects_head_dim_64_and_missing_scale():
     args[12] = 128
     args[3] = None
     assert lib.fmha_fwd_fp8pv(*args) == 1
+
+
+def test_fp4_argument_checks():
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    # q, k, v codes, exponents, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, heads, d, ...
+    args = [0x10000, 0x20000, 0x30000, 0x70000, None, None, 1, 128, 128, 128, 128, 2, 64, 0,
+            ctypes.c_float(0.125), 0x40000, 0x50000, None]
+    assert lib.fmha_fwd_fp4pv(*args) == 2          # head_dim 64
+    args[12] = 128
+    args[3] = None
+    assert lib.fmha_fwd_fp4pv(*args) == 1          # exponents missing
+    args[3] = 0x70002
+    assert lib.fmha_fwd_fp4pv(*args) == 1          # exponents not 4-byte aligned
+    args[3] = 0x70000
+    args[2] = 0x30008
+    assert lib.fmha_fwd_fp4pv(*args) == 1          # codes not 16-byte aligned
+    args[2] = 0x30000
+    vargs = args[:-1]
+    assert lib.fmha_fwd_fp4pv_variant(*vargs, 3, None) == 2   # no pipelined fp4 kernel
+    assert lib.fmha_fwd_fp4pv_variant(*vargs, 5, None) == 1
+    # nothing to compute: no launch, no GPU needed
+    empty = [None, None, None, None, None, None, 0, 0, 0, 0, 0, 2, 128, 1,
+             ctypes.c_float(0.125), None, None, None]
+    assert lib.fmha_fwd_fp4pv(*empty) == 0
 
 
 @pytest.mark.parametrize("cu,total,max_s,ok", [
