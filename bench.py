@@ -23,7 +23,8 @@ Extra objects on the same line:
                 the same workload (whole document x head units), in the same unit.
 
 Options: --workload c1|c2|c3|c4|c5 (other workloads, for measurement only:
-x_varlen_noncausal_32k, x_causal_fp4pv_32k),
+x_varlen_noncausal_32k, x_short_q_long_k, x_causal_fp4pv_32k), --splits N|auto
+(the split-KV pass),
 --variant, --no-cpu-baseline, --counters (a short run for rocprofv3 --pmc: a
 copy kernel of known size, then a few steps), --summarize-counters and
 --summarize-trace (turn rocprofv3 CSV output into the committed summaries).
@@ -69,10 +70,11 @@ def pv_format(w) -> int:
     return 2 if w.fp4_pv else 1 if w.fp8_pv else 0
 
 
-def kernel_template_name(w, variant):
+def kernel_template_name(w, variant, split=False):
     if variant == "pipelined":
         return f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}>"
-    return f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}, {pv_format(w)}>"
+    return (f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}, {pv_format(w)}, "
+            f"{str(split).lower()}>")
 
 
 def parse_args():
@@ -84,9 +86,12 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c4",
                     choices=sorted(SHORT) + sorted(SHORT.values()) +
-                    ["x_varlen_noncausal_32k", "x_causal_fp4pv_32k"])
+                    ["x_varlen_noncausal_32k", "x_short_q_long_k", "x_causal_fp4pv_32k"])
     ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong", "pipelined"],
                     help="kernel variant (auto picks by problem size)")
+    ap.add_argument("--splits", default=None,
+                    help="run the split-KV pass (bf16) with this many key splits, or 'auto'; "
+                         "the workspace is allocated once, outside the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-flop", type=float, default=CPU_SAMPLE_FLOP,
                     help="counted FLOP of the oracle sample (whole document x head units)")
@@ -121,9 +126,24 @@ def device_inputs(w, dev):
     return inp, d
 
 
-def make_step(w, d, variant="auto"):
+def make_step(w, d, variant="auto", splits=None):
     import head_attention_forward_fmha_amd as fm
+    import torch
     mq, mk = w.max_seqlen_q, w.max_seqlen_k
+    if splits is not None:
+        if w.fp8_pv or w.fp4_pv:
+            raise SystemExit("split-KV runs the bf16 path only")
+        n = (fm.splitkv_num_splits(w.batch, mq, mk, w.heads, w.causal, variant)
+             if splits == "auto" else int(splits))
+        nbytes = fm.splitkv_workspace_size(w.total_q, w.heads, w.head_dim, n)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=d["q"].device) if nbytes else None
+        d["splits"] = n
+
+        def step():
+            fm.fwd_splitkv(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], mq, mk, causal=w.causal,
+                           softmax_scale=w.softmax_scale, out=d["out"], lse=d["lse"],
+                           num_splits=n, workspace=ws, variant=variant)
+        return step
     if w.fp8_pv:
         def step():
             fm.fwd_fp8pv(d["q"], d["k"], d["v8"], d["vs"], d["cu_q"], d["cu_k"], mq, mk,
@@ -326,7 +346,7 @@ def main():
     w = {**WORKLOADS, **EXTRA_WORKLOADS}[name]
     dev = torch.device("cuda:0")
     inp, d = device_inputs(w, dev)
-    step = make_step(w, d, args.variant)
+    step = make_step(w, d, args.variant, args.splits)
     if args.counters:
         run_counters(w, d, step)
         return
@@ -334,7 +354,8 @@ def main():
     flops = w.flops()
     ms_per_step = total_ms / args.steps
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
-    # one launch per step: the per-step events bracket exactly one kernel
+    # one launch per step (split-KV: the split kernel and the merge): the per-step
+    # events bracket the whole pass
     launch_ms = sum(each) / len(each)
     achieved = flops / (launch_ms * 1e-3) / 1e12
     dtype = "bf16+fp8" if w.fp8_pv else "bf16+e2m1" if w.fp4_pv else "bf16"
@@ -343,7 +364,8 @@ def main():
                else fm.auto_variant(w.batch, w.max_seqlen_q, w.heads))
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": load_traffic(w, variant),
-            "kernel": kernel_template_name(w, variant), "launch_avg_us": round(launch_ms * 1e3, 2),
+            "kernel": kernel_template_name(w, variant, "splits" in d),
+            "launch_avg_us": round(launch_ms * 1e3, 2),
             "algorithmic_flop_per_launch": flops,
             "algorithmic_hbm_bytes_per_launch": w.hbm_bytes(),
             "algorithmic_hbm_gbps": round(w.hbm_bytes() / (launch_ms * 1e-3) / 1e9, 1)}
@@ -367,7 +389,7 @@ def main():
         "config": {"workload": w.description, "name": w.name, "total_tokens": w.total_q,
                    "docs": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "causal": w.causal, "seed": w.seed, "fp8_pv": w.fp8_pv, "fp4_pv": w.fp4_pv,
-                   "kernel_variant": variant},
+                   "kernel_variant": variant, "key_splits": d.get("splits", 1)},
         "roofline": roof,
         "cpu_baseline": None,
     }

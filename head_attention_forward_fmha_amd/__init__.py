@@ -21,7 +21,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import FMHA_OK, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
+__all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "fwd_splitkv", "splitkv_num_splits",
+           "splitkv_workspace_size", "merge_partials", "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
            "FmhaError", "EXPORTED_SYMBOLS", "VARIANTS", "load_library"]
 
 
@@ -193,6 +194,91 @@ def fwd_fp4pv(q, k, v_e2m1, v_mx_scale, cu_seqlens_q=None, cu_seqlens_k=None,
                                     ctypes.c_void_p(_stream_handle(dev)))
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_fwd_fp4pv")
+    return out, lse
+
+
+def splitkv_workspace_size(total_q: int, num_heads: int, head_dim: int, num_splits: int) -> int:
+    """Bytes of workspace fwd_splitkv needs (0 for invalid sizes)."""
+    return int(_lib.load().fmha_fwd_splitkv_workspace_size(int(total_q), int(num_heads),
+                                                            int(head_dim), int(num_splits)))
+
+
+def splitkv_num_splits(batch: int, max_seqlen_q: int, max_seqlen_k: int, num_heads: int,
+                       causal: bool = False, variant: str = "auto") -> int:
+    """The split count the library suggests for this problem on the current device."""
+    n = _lib.load().fmha_fwd_splitkv_num_splits(int(batch), int(max_seqlen_q), int(max_seqlen_k),
+                                                 int(num_heads), int(bool(causal)),
+                                                 VARIANTS[variant])
+    if n < 0:
+        raise ValueError("negative problem size or unknown variant")
+    return int(n)
+
+
+def fwd_splitkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None,
+                max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                causal: bool = False, softmax_scale: Optional[float] = None, out=None, lse=None,
+                return_lse: bool = True, num_splits="auto", workspace=None,
+                variant: str = "auto") -> Tuple:
+    """bf16 FMHA forward with the key range of each query block split num_splits
+    ways and the parts merged (same result as ``fwd``). ``workspace`` is a device
+    tensor of at least splitkv_workspace_size(...) bytes (allocated when None);
+    after the call it holds the fp32 O parts [S, total_q, h, d] followed by the
+    LSE parts [S, h, total_q]."""
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, q.dim(), dev)
+    _check_tensor("k", k, torch.bfloat16, q.dim(), dev)
+    _check_tensor("v", v, torch.bfloat16, q.dim(), dev)
+    s = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if k.shape != v.shape or k.shape[-2:] != q.shape[-2:]:
+        raise ValueError("k and v must match, with q's heads and head_dim")
+    if num_splits == "auto":
+        n_split = splitkv_num_splits(s["batch"], s["max_q"], s["max_k"], s["heads"], causal,
+                                     variant if variant != "pipelined" else "auto")
+    else:
+        n_split = int(num_splits)
+    scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
+    need = splitkv_workspace_size(s["total_q"], s["heads"], s["d"], n_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    st = lib.fmha_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(s["cu_q"]), _ptr(s["cu_k"]),
+                              s["batch"], s["total_q"], s["total_k"], s["max_q"], s["max_k"],
+                              s["heads"], s["d"], int(bool(causal)), ctypes.c_float(scale),
+                              _ptr(out), _ptr(lse), n_split, _ptr(workspace), ws_bytes,
+                              VARIANTS[variant],
+                              ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_fwd_splitkv")
+    return out, lse
+
+
+def merge_partials(o_part, lse_part, out=None, lse=None, return_lse: bool = True) -> Tuple:
+    """Merge fp32 partial results o_part [S, total_q, h, d] / lse_part [S, h, total_q]
+    over disjoint key ranges into bf16 out [total_q, h, d] and fp32 lse [h, total_q]."""
+    import torch
+    lib = _lib.load()
+    dev = o_part.device
+    _check_tensor("o_part", o_part, torch.float32, 4, dev)
+    _check_tensor("lse_part", lse_part, torch.float32, 3, dev)
+    n_parts, tq, h, d = o_part.shape
+    if tuple(lse_part.shape) != (n_parts, h, tq):
+        raise ValueError("lse_part must be [S, heads, total_q] matching o_part")
+    if out is None:
+        out = torch.empty((tq, h, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((h, tq), dtype=torch.float32, device=dev)
+    st = lib.fmha_merge_partials(_ptr(o_part), _ptr(lse_part), n_parts, tq, h, d, _ptr(out),
+                                 _ptr(lse), ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_merge_partials")
     return out, lse
 
 

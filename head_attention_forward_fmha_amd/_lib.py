@@ -27,6 +27,10 @@ EXPORTED_SYMBOLS = (
     "fmha_fwd_fp8pv_variant",
     "fmha_fwd_fp4pv",
     "fmha_fwd_fp4pv_variant",
+    "fmha_fwd_splitkv",
+    "fmha_fwd_splitkv_workspace_size",
+    "fmha_fwd_splitkv_num_splits",
+    "fmha_merge_partials",
     "fmha_fwd_auto_variant",
     "fmha_validate_cu_seqlens",
     "fmha_status_string",
@@ -84,6 +88,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmha_fwd_fp4pv.restype = ctypes.c_int
     lib.fmha_fwd_fp4pv_variant.argtypes = _FWD_FP8_ARGS[:-1] + [_i32, _vp]
     lib.fmha_fwd_fp4pv_variant.restype = ctypes.c_int
+    # split-KV: fmha_fwd_variant's arguments up to lse, then num_splits, workspace,
+    # workspace bytes, variant, stream
+    lib.fmha_fwd_splitkv.argtypes = _FWD_ARGS[:-1] + [_i32, _vp, ctypes.c_size_t, _i32, _vp]
+    lib.fmha_fwd_splitkv.restype = ctypes.c_int
+    lib.fmha_fwd_splitkv_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
+    lib.fmha_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fmha_fwd_splitkv_num_splits.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+    lib.fmha_fwd_splitkv_num_splits.restype = ctypes.c_int32
+    lib.fmha_merge_partials.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+    lib.fmha_merge_partials.restype = ctypes.c_int
     lib.fmha_fwd_auto_variant.argtypes = [_i32, _i32, _i32]
     lib.fmha_fwd_auto_variant.restype = ctypes.c_int32
     lib.fmha_validate_cu_seqlens.argtypes = [_vp, _i32, _i32, _i32]

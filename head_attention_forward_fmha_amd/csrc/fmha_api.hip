@@ -59,6 +59,7 @@ fmha::FwdParams make_params(const void* q, const void* k, const void* v, const i
   p.cu_q = cu_q;
   p.cu_k = cu_k;
   p.v_scale = nullptr;
+  p.num_splits = 1;
   p.out = out;
   p.lse = lse;
   p.batch = batch;
@@ -184,6 +185,79 @@ fmha_status_t fmha_fwd_fp4pv(const void* q, const void* k, const uint8_t* v_e2m1
                                 total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads,
                                 head_dim, causal, softmax_scale, out, lse, FMHA_VARIANT_AUTO,
                                 stream);
+}
+
+size_t fmha_fwd_splitkv_workspace_size(int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                       int32_t num_splits) {
+  if (total_q < 0 || num_heads <= 0 || (head_dim != 64 && head_dim != 128) || num_splits < 1 ||
+      num_splits > fmha::kMaxSplits)
+    return 0;
+  if (num_splits == 1) return 0;   // runs the unsplit pass, which needs no workspace
+  return (size_t)num_splits * (size_t)total_q * (size_t)num_heads * (size_t)(head_dim + 1) *
+         sizeof(float);
+}
+
+int32_t fmha_fwd_splitkv_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_heads, int32_t causal, int32_t variant) {
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads < 0) return -1;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PINGPONG) return -1;
+  return fmha::recommended_splits(batch, max_seqlen_q, max_seqlen_k, num_heads, causal != 0,
+                                  variant);
+}
+
+fmha_status_t fmha_fwd_splitkv(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads, int32_t head_dim,
+                               int32_t causal, float softmax_scale,
+                               void* out, float* lse, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t variant, void* stream) {
+  fmha_status_t st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
+                                  softmax_scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PIPELINED) return FMHA_ERR_INVALID_ARG;
+  if (variant == FMHA_VARIANT_PIPELINED) return FMHA_ERR_UNSUPPORTED;
+  if (num_splits < 1 || num_splits > fmha::kMaxSplits) return FMHA_ERR_INVALID_ARG;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
+  fmha::FwdParams p = make_params(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, softmax_scale, out, lse);
+  if (num_splits == 1) {
+    const hipError_t e = fmha::launch_fwd_bf16(p, head_dim, causal != 0, variant,
+                                               (hipStream_t)stream);
+    return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+  }
+  const size_t need = fmha_fwd_splitkv_workspace_size(total_q, num_heads, head_dim, num_splits);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+    return FMHA_ERR_INVALID_ARG;
+  p.num_splits = num_splits;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = p.o_part + (size_t)num_splits * total_q * num_heads * head_dim;
+  hipError_t e = fmha::launch_fwd_bf16_splitkv(p, head_dim, causal != 0, variant,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return FMHA_ERR_LAUNCH;
+  e = fmha::launch_merge_partials(p.o_part, p.lse_part, num_splits, total_q, num_heads, head_dim,
+                                  out, lse, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+fmha_status_t fmha_merge_partials(const float* o_part, const float* lse_part, int32_t num_parts,
+                                  int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                  void* out, float* lse, void* stream) {
+  if (num_parts < 1 || num_parts > fmha::kMaxSplits || total_q < 0 || num_heads <= 0)
+    return FMHA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return FMHA_ERR_UNSUPPORTED;
+  if ((int64_t)num_heads * total_q > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+  if (total_q == 0) return FMHA_OK;
+  if (o_part == nullptr || lse_part == nullptr || out == nullptr) return FMHA_ERR_INVALID_ARG;
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) || !aligned16(out) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return FMHA_ERR_INVALID_ARG;
+  hipError_t e = fmha::launch_merge_partials(o_part, lse_part, num_parts, total_q, num_heads,
+                                             head_dim, out, lse, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
 
 int32_t fmha_fwd_auto_variant(int32_t batch, int32_t max_seqlen_q, int32_t num_heads) {

@@ -219,8 +219,7 @@ __device__ __forceinline__ void align_keys_to_blocks(WorkItem& w) {
 // the next and the XCD finishes evenly.
 struct ItemCursor {
   int start, count, per_xcd, lane, round;
-  __device__ __forceinline__ explicit ItemCursor(const FwdParams& p) {
-    const int n_items = p.batch * p.heads * p.n_mblocks;
+  __device__ __forceinline__ explicit ItemCursor(int n_items) {
     const int xcd = blockIdx.x % kXcds;
     const int per = n_items / kXcds, extra = n_items % kXcds;
     start = xcd * per + min(xcd, extra);
@@ -246,9 +245,17 @@ struct ItemCursor {
 // Runs f(p, item) for this workgroup's work items. Persistent launches
 // (kPersistent) walk the XCD's range with an ItemCursor, re-reading the
 // parameters per item (kernel_params); the others take the single item their
-// block index names, with the same XCD-contiguous numbering.
-template <bool kPersistent, typename F>
+// block index names, with the same XCD-contiguous numbering. Split-KV launches
+// (kSplit) have num_splits items per (document, head, query block), adjacent.
+template <bool kPersistent, bool kSplit, typename F>
 __device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f);
+
+template <bool kSplit>
+__device__ __forceinline__ int n_work_items(const FwdParams& p) {
+  const int n = p.batch * p.heads * p.n_mblocks;
+  if constexpr (kSplit) return n * p.num_splits;
+  return n;
+}
 
 // The kernel's own FwdParams argument, read from the kernel-argument segment.
 // The persistent kernels fetch it afresh for every work item: the pointer passes
@@ -285,10 +292,10 @@ __device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int bm,
   return w;
 }
 
-template <bool kPersistent, typename F>
+template <bool kPersistent, bool kSplit, typename F>
 __device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f) {
   if constexpr (kPersistent) {
-    ItemCursor cursor(params);
+    ItemCursor cursor(n_work_items<kSplit>(params));
     int item;
     bool first = true;
     while (cursor.next(item)) {
@@ -299,7 +306,7 @@ __device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f) {
       f(kernel_params(), item);
     }
   } else {
-    const int n_items = params.batch * params.heads * params.n_mblocks;
+    const int n_items = n_work_items<kSplit>(params);
     const int xcd = blockIdx.x % kXcds;
     const int per = n_items / kXcds, extra = n_items % kXcds;
     f(params, xcd * per + min(xcd, extra) + (int)blockIdx.x / kXcds);
@@ -1046,6 +1053,36 @@ struct WaveTile {
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
     return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  }
+
+  // Split-KV (bf16 path): split `split`'s O, normalised by its own row sum, and
+  // its LSE, both fp32, into the partial buffers. A row that saw no key of this
+  // split gets O = 0 and LSE = -inf, which the merge weighs by zero.
+  __device__ __forceinline__ void epilogue_partial(const FwdParams& p, const WorkItem& w,
+                                                   int split) {
+    static_assert(!kFp8 && !kFp4, "split-KV runs the bf16 path");
+    l_run = wave_half_swap_sum(l_run);
+    if (qi >= w.sq) return;
+    const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
+    const size_t row = (size_t)split * p.total_q + (size_t)(w.q_start + qi);
+    float* op = p.o_part + (row * p.heads + w.head) * kD;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int d0 = 32 * db + 8 * ig + 4 * half;
+        float4 o4;
+        o4.x = oacc[db][4 * ig + 0] * inv_l;
+        o4.y = oacc[db][4 * ig + 1] * inv_l;
+        o4.z = oacc[db][4 * ig + 2] * inv_l;
+        o4.w = oacc[db][4 * ig + 3] * inv_l;
+        *(float4*)(op + d0) = o4;
+      }
+    if (half == 0) {
+      float lse = -__builtin_inff();
+      if (l_run > 0.f) lse = (m_run * c + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
+      p.lse_part[((size_t)split * p.heads + w.head) * p.total_q + w.q_start + qi] = lse;
+    }
   }
 
   // O /= l -> bf16 store; LSE = scale*m + ln(l) (natural log). A row with no

@@ -30,13 +30,30 @@
 
 namespace fmha {
 
+// ---------------------------------------------------------------- split-KV
+
+// Split-KV: split s of num_splits takes key tiles [t0, t1) of the n_tiles the
+// work item would visit, t0 = s*n/num_splits. The item's key window is moved
+// to start at tile t0 (k_start and sk shrink by the same amount, and so does
+// the causal offset sk - sq, so every mask keeps its meaning); the split then
+// visits t1 - t0 tiles from there. Returns t1 - t0.
+__device__ __forceinline__ int take_split(WorkItem& w, int& causal_off, int n_tiles, int split,
+                                          int num_splits) {
+  const int t0 = (int)((long long)split * n_tiles / num_splits);
+  const int t1 = (int)((long long)(split + 1) * n_tiles / num_splits);
+  w.k_start += t0 * kBN;
+  w.sk -= t0 * kBN;
+  causal_off -= t0 * kBN;
+  return t1 - t0;
+}
+
 // ---------------------------------------------------------------- 4-wave kernel
 
 constexpr int kWaves4 = 4;
 constexpr int kBM4 = kWaves4 * 32;  // query rows per workgroup
 static_assert(kBM4 == kRowsFourWave, "4-wave block height");
 
-template <int kD, bool kCausal, int kPv>
+template <int kD, bool kCausal, int kPv, bool kSplit>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves4 * 64, kWaves4 * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fmha_fwd_kernel(FwdParams params) {
@@ -45,13 +62,19 @@ void fmha_fwd_kernel(FwdParams params) {
   __shared__ __attribute__((aligned(1024))) char smem_v[2][WT::kVStageBytes];
 
   auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
+  int split = 0;
+  if constexpr (kSplit) {
+    split = item % p.num_splits;
+    item /= p.num_splits;
+  }
   WorkItem w = decode_work_item(p, kBM4, item);
   if (w.m0 >= w.sq) return;  // uniform over the workgroup
   if constexpr (WT::kFp4) align_keys_to_blocks(w);
-  const int causal_off = w.sk - w.sq;
+  int causal_off = w.sk - w.sq;
   int kend = w.sk;
   if (kCausal) kend = min(w.sk, max(0, w.m0 + kBM4 + causal_off));
-  const int n_tiles = (kend + kBN - 1) / kBN;
+  int n_tiles = (kend + kBN - 1) / kBN;
+  if constexpr (kSplit) n_tiles = take_split(w, causal_off, n_tiles, split, p.num_splits);
 
   const int wave = threadIdx.x >> 6;
   WT t;
@@ -93,9 +116,10 @@ void fmha_fwd_kernel(FwdParams params) {
   }
   if (j < n_tiles) step(j, std::integral_constant<int, 0>());
 
-  t.epilogue(p, w);
+  if constexpr (kSplit) t.epilogue_partial(p, w, split);
+  else t.epilogue(p, w);
   };
-  for_each_item<kCausal>(params, run_item);
+  for_each_item<kCausal, kSplit>(params, run_item);
 }
 
 // ---------------------------------------------------------------- 8-wave ping-pong kernel
@@ -112,7 +136,7 @@ struct NoPhaseTrace {
   __device__ __forceinline__ void mark(int /*event*/) {}
 };
 
-template <int kD, bool kCausal, int kPv, typename Trace = NoPhaseTrace>
+template <int kD, bool kCausal, int kPv, bool kSplit, typename Trace = NoPhaseTrace>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves8 * 64, kWaves8 * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void fmha_fwd_pingpong_kernel(FwdParams params) {
@@ -123,13 +147,19 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   __shared__ __attribute__((aligned(1024))) char smem_v[kStages8][WT::kVStageBytes];
 
   auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
+  int split = 0;
+  if constexpr (kSplit) {
+    split = item % p.num_splits;
+    item /= p.num_splits;
+  }
   WorkItem w = decode_work_item(p, kBM8, item);
   if (w.m0 >= w.sq) return;  // uniform over the workgroup
   if constexpr (WT::kFp4) align_keys_to_blocks(w);
-  const int causal_off = w.sk - w.sq;
+  int causal_off = w.sk - w.sq;
   int kend = w.sk;
   if (kCausal) kend = min(w.sk, max(0, w.m0 + kBM8 + causal_off));
-  const int n = (kend + kBN - 1) / kBN;
+  int n = (kend + kBN - 1) / kBN;
+  if constexpr (kSplit) n = take_split(w, causal_off, n, split, p.num_splits);
 
   const int wave = threadIdx.x >> 6;
   const int grp = wave >> 2;  // 0: group A, 1: group B (half a tile behind)
@@ -220,9 +250,10 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   if (j <= n) slot_pair(j, std::integral_constant<int, 0>());
   if (j + 1 <= n) slot_pair(j + 1, std::integral_constant<int, 1>());
 
-  t.epilogue(p, w);
+  if constexpr (kSplit) t.epilogue_partial(p, w, split);
+  else t.epilogue(p, w);
   };
-  for_each_item<kCausal>(params, run_item);
+  for_each_item<kCausal, kSplit>(params, run_item);
 }
 
 // ---------------------------------------------------------------- pipelined kernel
@@ -337,7 +368,7 @@ void fmha_fwd_pipe_kernel(FwdParams params) {
 
   t.epilogue(p, w);
   };
-  for_each_item<kCausal>(params, run_item);
+  for_each_item<kCausal, false>(params, run_item);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -360,14 +391,15 @@ static int device_cus() {
   return cus;
 }
 
-template <int kD, bool kCausal, int kPv>
+template <int kD, bool kCausal, int kPv, bool kSplit = false>
 static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   FwdParams q = p;
   const int variant_run = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads);
   const bool use8 = variant_run == kVariantPingPong;
   const int bm = use8 ? kBM8 : kBM4;
   q.n_mblocks = (p.max_seqlen_q + bm - 1) / bm;
-  const long long n_items = (long long)q.n_mblocks * p.heads * p.batch;
+  if (!kSplit) q.num_splits = 1;
+  const long long n_items = (long long)q.n_mblocks * p.heads * p.batch * q.num_splits;
   if (n_items == 0) return hipSuccess;
   if (n_items > 0x7fffffffLL) return hipErrorInvalidValue;
   // causal kernels are persistent: as many workgroups as the chip holds at once
@@ -377,16 +409,16 @@ static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   const long long grid =
       kCausal ? (std::min(n_items, resident) + kXcds - 1) / kXcds * kXcds : n_items;
   if (variant_run == kVariantPipelined) {
-    if constexpr (kPv == kPvBf16)
+    if constexpr (kPv == kPvBf16 && !kSplit)
       hipLaunchKernelGGL((fmha_fwd_pipe_kernel<kD, kCausal>), dim3((unsigned)grid),
                          dim3(kWavesPipe * 64), 0, stream, q);
     else
       return hipErrorInvalidValue;
   } else if (use8)
-    hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<kD, kCausal, kPv>), dim3((unsigned)grid),
-                       dim3(kWaves8 * 64), 0, stream, q);
+    hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<kD, kCausal, kPv, kSplit>),
+                       dim3((unsigned)grid), dim3(kWaves8 * 64), 0, stream, q);
   else
-    hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kPv>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((fmha_fwd_kernel<kD, kCausal, kPv, kSplit>), dim3((unsigned)grid),
                        dim3(kWaves4 * 64), 0, stream, q);
   return hipGetLastError();
 }
@@ -412,6 +444,55 @@ hipError_t launch_fwd_fp4pv(const FwdParams& p, int head_dim, bool causal, int v
   if (head_dim != 128) return hipErrorInvalidValue;
   return causal ? launch<128, true, kPvE2m1>(p, variant, stream)
                 : launch<128, false, kPvE2m1>(p, variant, stream);
+}
+
+hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int head_dim, bool causal, int variant,
+                                   hipStream_t stream) {
+  if (p.num_splits < 1 || p.num_splits > kMaxSplits) return hipErrorInvalidValue;
+  if (head_dim == 128)
+    return causal ? launch<128, true, kPvBf16, true>(p, variant, stream)
+                  : launch<128, false, kPvBf16, true>(p, variant, stream);
+  return causal ? launch<64, true, kPvBf16, true>(p, variant, stream)
+                : launch<64, false, kPvBf16, true>(p, variant, stream);
+}
+
+// Split count for a problem: the one that minimises the estimated time
+//   rounds(S) * (tiles / S + kOverheadTiles) * tile_us + merge_us(S)   (S > 1)
+// where rounds(S) is how many times the resident workgroups must be refilled
+// to run items * S work items, tile_us the time of one 64-key step of a work
+// item with the device full (about 4 TFLOP/s per compute unit), kOverheadTiles
+// a work item's prologue and epilogue, and merge_us the merge pass (reading S
+// fp32 partial rows at about 5 TB/s). A split must beat the unsplit estimate by
+// 15%: a partly idle device runs each busy compute unit faster than the model
+// assumes, which favours not splitting.
+int recommended_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t heads, bool causal, int variant) {
+  if (batch <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 || heads <= 0) return 1;
+  const int v = resolve_variant(variant, batch, max_seqlen_q, heads);
+  const bool use8 = v == kVariantPingPong;
+  const int bm = use8 ? kBM8 : kBM4;
+  const int wgs_per_cu = use8 ? 1 : 2;
+  const long long slots = (long long)device_cus() * wgs_per_cu;
+  const long long items = (long long)(max_seqlen_q + bm - 1) / bm * heads * batch;
+  // a causal item visits half the keys on average
+  const double tiles = (double)((max_seqlen_k + kBN - 1) / kBN) / (causal ? 2.0 : 1.0);
+  const double d = 128.0;   // the time per tile scales with head_dim the same way for both
+  const double tile_us = 4.0 * bm * kBN * d * wgs_per_cu / 4.0e12 * 1e6;
+  const double rows = (double)batch * max_seqlen_q * heads;
+  constexpr double kOverheadTiles = 3.5;
+  const double unsplit = (double)((items + slots - 1) / slots) * (tiles + kOverheadTiles) * tile_us;
+  int best = 1;
+  double best_cost = unsplit;
+  for (int s = 2; s <= 16 && s <= tiles; ++s) {
+    const double rounds = (double)((items * s + slots - 1) / slots);
+    const double merge_us = 3.0 + rows * d * 4.0 * (s + 0.5) / 5.0e12 * 1e6;
+    const double cost = rounds * (tiles / s + kOverheadTiles) * tile_us + merge_us;
+    if (cost < best_cost && cost < 0.85 * unsplit) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 }  // namespace fmha

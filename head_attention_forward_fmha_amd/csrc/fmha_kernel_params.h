@@ -25,6 +25,11 @@ struct FwdParams {
   int32_t heads;
   float scale_log2;       // softmax_scale * log2(e)
   int32_t n_mblocks;      // query blocks per document (set by the launcher)
+  // split-KV: the key tiles of every work item are cut into num_splits ranges,
+  // each writing its own O (fp32, normalised by its own row sum) and LSE
+  int32_t num_splits;     // 1 unless launched by launch_fwd_bf16_splitkv
+  float* o_part;          // [num_splits, total_q, heads, d]
+  float* lse_part;        // [num_splits, heads, total_q]
 };
 
 // Number formats of the P.V product: bf16, fp8 e4m3 (one fp32 scale per head
@@ -61,6 +66,18 @@ hipError_t launch_fwd_fp8pv(const FwdParams& p, int head_dim, bool causal, int v
                             hipStream_t stream);
 hipError_t launch_fwd_fp4pv(const FwdParams& p, int head_dim, bool causal, int variant,
                             hipStream_t stream);
+// bf16 forward pass with the key tiles of each work item cut into p.num_splits
+// ranges: writes p.o_part / p.lse_part, not p.out / p.lse (see launch_merge_partials)
+hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int head_dim, bool causal, int variant,
+                                   hipStream_t stream);
+// out[t, h, :] = sum_s exp(LSE_s - LSE) O_s[t, h, :] (bf16), LSE = log sum_s exp(LSE_s)
+hipError_t launch_merge_partials(const float* o_part, const float* lse_part, int num_parts,
+                                 int total_q, int heads, int head_dim, void* out, float* lse,
+                                 hipStream_t stream);
+// split count the automatic choice uses for a problem on the current device
+int recommended_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t heads, bool causal, int variant);
+constexpr int kMaxSplits = 64;
 
 }  // namespace fmha
 

@@ -46,6 +46,7 @@
 #ifndef FMHA_H_
 #define FMHA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -185,6 +186,66 @@ fmha_status_t fmha_fwd_fp4pv_variant(const void* q, const void* k, const uint8_t
                                      void* out, float* lse, int32_t variant, void* stream);
 
 /*
+ * Split-KV forward pass (bf16): the same function as fmha_fwd_variant, for
+ * problems with too few query blocks to fill the GPU (short query ranges
+ * against long keys). The key tiles each (document, head, query block) visits
+ * are cut into num_splits near-equal ranges; each range runs as its own work
+ * item and writes its O (fp32, normalised by its own row sum) and LSE into the
+ * workspace; a second kernel merges them (as fmha_merge_partials) into out and
+ * lse on the same stream.
+ *   num_splits       1 .. 64 (fmha_fwd_splitkv_num_splits suggests one); 1 runs
+ *                    the unsplit pass (fmha_fwd_variant) and needs no workspace
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    fmha_fwd_splitkv_workspace_size(...) bytes, owned by the
+ *                    caller (NULL allowed when num_splits is 1); contents on
+ *                    return when num_splits > 1: O parts fp32
+ *                    [num_splits, total_q, num_heads, head_dim], then LSE parts
+ *                    fp32 [num_splits, num_heads, total_q]. Calls that share a
+ *                    workspace must not overlap.
+ *   variant          FMHA_VARIANT_AUTO, _FOUR_WAVE or _PINGPONG (_PIPELINED:
+ *                    FMHA_ERR_UNSUPPORTED)
+ * Every other argument as for fmha_fwd.
+ */
+fmha_status_t fmha_fwd_splitkv(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads, int32_t head_dim,
+                               int32_t causal, float softmax_scale,
+                               void* out, float* lse, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t variant, void* stream);
+
+/* Bytes of workspace fmha_fwd_splitkv needs: num_splits * total_q * num_heads *
+ * (head_dim + 1) * 4 when num_splits > 1, 0 when num_splits is 1 or a size is
+ * invalid. Host only. */
+size_t fmha_fwd_splitkv_workspace_size(int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                       int32_t num_splits);
+
+/* The split count that minimises the estimated time of a problem on the current
+ * HIP device (1: do not split); -1 for negative sizes or an unknown variant.
+ * Queries the device's compute-unit count once; launches nothing. */
+int32_t fmha_fwd_splitkv_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_heads, int32_t causal, int32_t variant);
+
+/*
+ * Merges partial attention results over disjoint key ranges of the same query
+ * rows (the combine step of split-KV, and of a key-sharded, context-parallel
+ * pass after the parts are gathered):
+ *   LSE = log sum_s exp(LSE_s),  out = sum_s exp(LSE_s - LSE) * O_s  (bf16)
+ * Parts with LSE_s = -inf (no key) weigh nothing; a row with no key anywhere
+ * gets out = 0, LSE = -inf.
+ *   o_part    fp32 [num_parts, total_q, num_heads, head_dim], 16-byte aligned
+ *   lse_part  fp32 [num_parts, num_heads, total_q] (natural log)
+ *   out       bf16 [total_q, num_heads, head_dim], 16-byte aligned
+ *   lse       fp32 [num_heads, total_q], or NULL
+ *   num_parts 1 .. 64; head_dim 64 or 128
+ */
+fmha_status_t fmha_merge_partials(const float* o_part, const float* lse_part, int32_t num_parts,
+                                  int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                  void* out, float* lse, void* stream);
+
+/*
  * The kernel variant FMHA_VARIANT_AUTO resolves to for a problem of `batch`
  * documents, longest query document max_seqlen_q and num_heads heads:
  * FMHA_VARIANT_FOUR_WAVE or FMHA_VARIANT_PINGPONG. Negative sizes give -1.
@@ -206,7 +267,7 @@ const char* fmha_status_string(fmha_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int32_t fmha_abi_version(void);
 
-#define FMHA_ABI_VERSION ((1 << 16) | 1)
+#define FMHA_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

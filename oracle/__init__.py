@@ -19,12 +19,16 @@ Parity status per function:
       every scaled P is an e2m1 value, closed forms for a dropped key and a
       single visible key, the log-domain fold against post-exp division, group
       locality, and the error bound against attention_fp4pv).
+  merge_partials -- pinned (attention over disjoint key ranges, each taken
+      with the oracle's own masked softmax, merges to attention over all keys;
+      empty ranges and empty rows).
 """
 
 from .reference import (DEFAULT_ROW_BLOCK, attention, attention_bruteforce, attention_rows,
                         attention_sampled, scores, softmax_rows, visible)
 from .fp8 import (E4M3_MAX, attention_fp8pv, attention_fp8pv_emulated, attention_fp8pv_sampled,
                   dequantize_v, e4m3_decode, e4m3_encode)
+from .merge import merge_partials
 from .fp4 import (E2M1_MAX, FP4Emulation, attention_fp4pv, attention_fp4pv_bruteforce,
                   attention_fp4pv_emulated, attention_fp4pv_sampled, e2m1_decode, e2m1_encode,
                   mx_dequantize_v)
@@ -35,5 +39,5 @@ __all__ = [
     "attention_fp8pv_emulated", "attention_fp8pv_sampled", "dequantize_v", "e4m3_decode",
     "e4m3_encode", "E2M1_MAX", "FP4Emulation", "attention_fp4pv", "attention_fp4pv_bruteforce",
     "attention_fp4pv_emulated", "attention_fp4pv_sampled", "e2m1_decode", "e2m1_encode",
-    "mx_dequantize_v",
+    "mx_dequantize_v", "merge_partials",
 ]

@@ -131,12 +131,16 @@ WORKLOADS = {
 }
 
 # Extra shapes for measurement only (not among the five above): the c4 token
-# layout without the causal mask, which isolates the cost of causal scheduling,
-# and the c5 shape with P.V in fp4 (MXFP4 V, per-group e2m1 P).
+# layout without the causal mask, which isolates the cost of causal scheduling;
+# a short query range against long keys (few query blocks: the shape split-KV
+# is for); and the c5 shape with P.V in fp4 (MXFP4 V, per-group e2m1 P).
 EXTRA_WORKLOADS = {
     "x_varlen_noncausal_32k": Workload(
         "x_varlen_noncausal_32k", "varlen non-causal: 32768 tokens / 8 docs, h=32 d=128",
         heads=32, head_dim=128, causal=False, doc_lens=_linspace_docs(32768, 8)),
+    "x_short_q_long_k": Workload(
+        "x_short_q_long_k", "short queries, long keys: 512 query rows x 32768 keys, h=16 d=128, "
+        "no mask", heads=16, head_dim=128, causal=False, doc_lens=((512, 32768),)),
     "x_causal_fp4pv_32k": Workload(
         "x_causal_fp4pv_32k", "single-doc causal fp4 P.V: 32768 tokens, h=16 d=128",
         heads=16, head_dim=128, causal=True, doc_lens=_linspace_docs(32768, 1), fp4_pv=True),

@@ -25,6 +25,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["fmha_fwd", "fmha_fwd_fp8pv", "fmha_fwd_variant",
                             "fmha_fwd_fp8pv_variant", "fmha_fwd_fp4pv", "fmha_fwd_fp4pv_variant",
+                            "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size",
+                            "fmha_fwd_splitkv_num_splits", "fmha_merge_partials",
                             "fmha_fwd_auto_variant", "fmha_validate_cu_seqlens",
                             "fmha_status_string", "fmha_abi_version"])
 
@@ -35,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert set(fm.EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert fm.abi_version() == (1 << 16) | 1
+    assert fm.abi_version() == (1 << 16) | 2
 
 
 def test_status_strings():
@@ -157,6 +159,55 @@ def test_fp4_argument_checks():
     empty = [None, None, None, None, None, None, 0, 0, 0, 0, 0, 2, 128, 1,
              ctypes.c_float(0.125), None, None, None]
     assert lib.fmha_fwd_fp4pv(*empty) == 0
+
+
+def test_splitkv_argument_checks():
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    assert fm.splitkv_workspace_size(2225, 16, 128, 3) == 3 * 2225 * 16 * 129 * 4
+    assert fm.splitkv_workspace_size(10, 2, 96, 2) == 0
+    assert fm.splitkv_workspace_size(10, 2, 64, 0) == 0
+    assert fm.splitkv_workspace_size(10, 2, 64, 65) == 0
+    base = [0x10000, 0x20000, 0x30000, None, None, 1, 128, 128, 128, 128, 2, 64, 0,
+            ctypes.c_float(0.125), 0x40000, 0x50000]
+    need = fm.splitkv_workspace_size(128, 2, 64, 2)
+    ok_tail = [2, 0x80000, need, 0, None]
+    for i, bad, status in ((0, 0, 1), (0, 65, 1), (1, None, 1), (1, 0x80008, 1),
+                           (2, need - 1, 1), (3, 3, 2), (3, 9, 1)):
+        tail = list(ok_tail)
+        tail[i] = bad
+        assert lib.fmha_fwd_splitkv(*base, *tail) == status, (i, bad)
+    # nothing to compute: no launch, workspace not needed
+    empty = [None, None, None, None, None, 0, 0, 0, 0, 0, 2, 64, 0, ctypes.c_float(0.125),
+             None, None]
+    assert lib.fmha_fwd_splitkv(*empty, 2, None, 0, 0, None) == 0
+    # merge: part count, head_dim, alignment
+    margs = [0x10000, 0x20000, 2, 100, 4, 128, 0x30000, 0x40000, None]
+    for i, bad, status in ((2, 0, 1), (2, 65, 1), (5, 96, 2), (0, 0x10008, 1), (6, 0x30008, 1),
+                           (1, 0x20002, 1), (0, None, 1)):
+        a = list(margs)
+        a[i] = bad
+        assert lib.fmha_merge_partials(*a) == status, (i, bad)
+    a = list(margs)
+    a[3] = 0
+    assert lib.fmha_merge_partials(*a) == 0
+
+
+def test_splitkv_num_splits_choice():
+    import head_attention_forward_fmha_amd as fm
+    # one value per size; splitting pays only when the query blocks do not fill the device
+    c4 = fm.splitkv_num_splits(8, 4096, 4096, 32, causal=True)
+    assert c4 == 1
+    # c2's 144 blocks of 256 rows: measured, splitting does not pay (the split
+    # items' overheads and the merge outweigh the idle compute units)
+    assert fm.splitkv_num_splits(1, 2225, 2225, 16) == 1
+    assert fm.splitkv_num_splits(1, 512, 32768, 16) >= 4  # short queries, long keys
+    assert fm.splitkv_num_splits(1, 64, 8192, 8) > 4      # few query rows, long keys
+    assert fm.splitkv_num_splits(1, 128, 64, 2) == 1      # a single key tile cannot split
+    with pytest.raises(ValueError):
+        fm.splitkv_num_splits(-1, 10, 10, 1)
+    with pytest.raises(ValueError):
+        fm.splitkv_num_splits(1, 10, 10, 1, variant="pipelined")
 
 
 @pytest.mark.parametrize("cu,total,max_s,ok", [
