@@ -362,6 +362,11 @@ def main():
     peak = MI355X_PEAK_TFLOPS["bf16"]
     variant = (args.variant if args.variant != "auto"
                else fm.auto_variant(w.batch, w.max_seqlen_q, w.heads))
+    if args.variant == "auto" and d.get("splits", 1) > 1:
+        # the library's automatic choice counts split work items: the 8-wave
+        # kernel from 128 items of 256 query rows
+        items = -(-w.max_seqlen_q // 256) * w.heads * w.batch * d["splits"]
+        variant = "pingpong" if items >= 128 else "four_wave"
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": load_traffic(w, variant),
             "kernel": kernel_template_name(w, variant, "splits" in d),

@@ -394,11 +394,11 @@ static int device_cus() {
 template <int kD, bool kCausal, int kPv, bool kSplit = false>
 static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   FwdParams q = p;
-  const int variant_run = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads);
+  if (!kSplit) q.num_splits = 1;
+  const int variant_run = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads, q.num_splits);
   const bool use8 = variant_run == kVariantPingPong;
   const int bm = use8 ? kBM8 : kBM4;
   q.n_mblocks = (p.max_seqlen_q + bm - 1) / bm;
-  if (!kSplit) q.num_splits = 1;
   const long long n_items = (long long)q.n_mblocks * p.heads * p.batch * q.num_splits;
   if (n_items == 0) return hipSuccess;
   if (n_items > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -468,28 +468,32 @@ hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int head_dim, bool causal
 int recommended_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                        int32_t heads, bool causal, int variant) {
   if (batch <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 || heads <= 0) return 1;
-  const int v = resolve_variant(variant, batch, max_seqlen_q, heads);
-  const bool use8 = v == kVariantPingPong;
-  const int bm = use8 ? kBM8 : kBM4;
-  const int wgs_per_cu = use8 ? 1 : 2;
-  const long long slots = (long long)device_cus() * wgs_per_cu;
-  const long long items = (long long)(max_seqlen_q + bm - 1) / bm * heads * batch;
   // a causal item visits half the keys on average
   const double tiles = (double)((max_seqlen_k + kBN - 1) / kBN) / (causal ? 2.0 : 1.0);
-  const double d = 128.0;   // the time per tile scales with head_dim the same way for both
-  const double tile_us = 4.0 * bm * kBN * d * wgs_per_cu / 4.0e12 * 1e6;
+  const double d = 128.0;   // tile and merge times both scale with head_dim
   const double rows = (double)batch * max_seqlen_q * heads;
   constexpr double kOverheadTiles = 3.5;
-  const double unsplit = (double)((items + slots - 1) / slots) * (tiles + kOverheadTiles) * tile_us;
+  // estimated time of s splits, on the kernel the launch would pick for them
+  auto cost = [&](int s) {
+    const int v = resolve_variant(variant, batch, max_seqlen_q, heads, s);
+    const bool use8 = v == kVariantPingPong;
+    const int bm = use8 ? kBM8 : kBM4;
+    const int wgs_per_cu = use8 ? 1 : 2;
+    const long long slots = (long long)device_cus() * wgs_per_cu;
+    const long long items = (long long)(max_seqlen_q + bm - 1) / bm * heads * batch * s;
+    const double tile_us = 4.0 * bm * kBN * d * wgs_per_cu / 4.0e12 * 1e6;
+    const double rounds = (double)((items + slots - 1) / slots);
+    const double merge_us = s > 1 ? 3.0 + rows * d * 4.0 * (s + 0.5) / 5.0e12 * 1e6 : 0.0;
+    return rounds * (tiles / s + kOverheadTiles) * tile_us + merge_us;
+  };
+  const double unsplit = cost(1);
   int best = 1;
   double best_cost = unsplit;
   for (int s = 2; s <= 16 && s <= tiles; ++s) {
-    const double rounds = (double)((items * s + slots - 1) / slots);
-    const double merge_us = 3.0 + rows * d * 4.0 * (s + 0.5) / 5.0e12 * 1e6;
-    const double cost = rounds * (tiles / s + kOverheadTiles) * tile_us + merge_us;
-    if (cost < best_cost && cost < 0.85 * unsplit) {
+    const double c = cost(s);
+    if (c < best_cost && c < 0.85 * unsplit) {
       best = s;
-      best_cost = cost;
+      best_cost = c;
     }
   }
   return best;

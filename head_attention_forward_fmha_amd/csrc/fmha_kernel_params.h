@@ -50,13 +50,14 @@ constexpr int kRowsPingPong = 256;
 constexpr int kRowsPipelined = 128;
 
 // The kernel a launch runs. Automatic selection takes the 8-wave kernel once the
-// problem has at least 128 blocks of 256 query rows (half the CUs of an
-// MI355X), else the 4-wave kernel, whose smaller blocks spread a small problem
-// over more CUs.
-inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int32_t heads) {
+// problem has at least 128 work items of 256 query rows (half the CUs of an
+// MI355X; a split-KV launch has `splits` items per block), else the 4-wave
+// kernel, whose smaller blocks spread a small problem over more CUs.
+inline int resolve_variant(int variant, int32_t batch, int32_t max_seqlen_q, int32_t heads,
+                           int splits = 1) {
   if (variant != kVariantAuto) return variant;
   const long long blocks = ((long long)max_seqlen_q + kRowsPingPong - 1) / kRowsPingPong *
-                           heads * batch;
+                           heads * batch * splits;
   return blocks >= 128 ? kVariantPingPong : kVariantFourWave;
 }
 

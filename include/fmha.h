@@ -144,7 +144,8 @@ fmha_status_t fmha_fwd_fp4pv(const void* q, const void* k, const uint8_t* v_e2m1
 /*
  * Kernel variant selection, for testing and tuning. FMHA_VARIANT_AUTO (what
  * fmha_fwd, fmha_fwd_fp8pv and fmha_fwd_fp4pv use) takes the 8-wave ping-pong kernel when the
- * problem has at least 128 blocks of 256 query rows, else the 4-wave kernel.
+ * problem has at least 128 blocks of 256 query rows, else the 4-wave kernel;
+ * fmha_fwd_splitkv counts each block num_splits times.
  * All variants compute the same function. They currently run the same per-row
  * arithmetic in the same key-tile order and give bit-identical results; the ABI
  * promises only agreement within rounding.
