@@ -24,7 +24,7 @@ Extra objects on the same line:
 
 Options: --workload c1|c2|c3|c4|c5 (other workloads, for measurement only:
 x_varlen_noncausal_32k, x_short_q_long_k, x_causal_fp4pv_32k), --splits N|auto
-(the split-KV pass),
+(the split-KV pass), --trace coarse|detailed (pipeline summary of a traced launch),
 --variant, --no-cpu-baseline, --counters (a short run for rocprofv3 --pmc: a
 copy kernel of known size, then a few steps), --summarize-counters and
 --summarize-trace (turn rocprofv3 CSV output into the committed summaries).
@@ -92,6 +92,9 @@ def parse_args():
     ap.add_argument("--splits", default=None,
                     help="run the split-KV pass (bf16) with this many key splits, or 'auto'; "
                          "the workspace is allocated once, outside the timed region")
+    ap.add_argument("--trace", choices=["coarse", "detailed"], default=None,
+                    help="after the warm-up, one traced launch of the causal ping-pong kernel; "
+                         "prints the pipeline summary instead of the throughput line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-flop", type=float, default=CPU_SAMPLE_FLOP,
                     help="counted FLOP of the oracle sample (whole document x head units)")
@@ -253,6 +256,37 @@ def run_counters(w, d, step):
     print(json.dumps({"counters_run": w.name, "copy_bytes": n, "steps": 3}), flush=True)
 
 
+def run_trace(w, d, step, args):
+    """Warm up untraced, then one traced launch; print the pipeline summary."""
+    import head_attention_forward_fmha_amd as fm
+    import numpy as np
+    import torch
+    from head_attention_forward_fmha_amd import pipeline_trace
+    if not w.causal or w.head_dim != 128:
+        raise SystemExit("the pipeline trace covers causal d=128 launches")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pv = "e4m3" if w.fp8_pv else "e2m1" if w.fp4_pv else "bf16"
+    v = d["v8"] if w.fp8_pv else d["v4"] if w.fp4_pv else d["v"]
+    vs = d["vs"] if w.fp8_pv else d["vx"] if w.fp4_pv else None
+    def traced():
+        return fm.fwd_trace(d["q"], d["k"], v, d["cu_q"], d["cu_k"], w.max_seqlen_q,
+                            w.max_seqlen_k, pv=pv, v_scale=vs, softmax_scale=w.softmax_scale,
+                            detailed=args.trace == "detailed", traced_workgroups=32)
+    traced()                       # loads the traced kernel's code
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    _, _, trace = traced()
+    end.record()
+    torch.cuda.synchronize()
+    summary = pipeline_trace.summarize(trace.cpu().numpy().view(np.uint64))
+    summary.update({"trace": args.trace, "workload": w.name, "pv": pv, "traced_workgroups": 32,
+                    "launch_us": round(start.elapsed_time(end) * 1e3, 1)})
+    print(json.dumps(summary), flush=True)
+
+
 def _counter_rows(path):
     import csv
     with open(path) as f:
@@ -349,6 +383,9 @@ def main():
     step = make_step(w, d, args.variant, args.splits)
     if args.counters:
         run_counters(w, d, step)
+        return
+    if args.trace:
+        run_trace(w, d, step, args)
         return
     total_ms, each = time_steps(step, args.steps, args.warmup)
     flops = w.flops()

@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import FMHA_OK, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
 
 __all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "fwd_splitkv", "splitkv_num_splits",
-           "splitkv_workspace_size", "merge_partials", "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
+           "splitkv_workspace_size", "merge_partials", "fwd_trace", "TRACE_EVENTS_PER_WAVE",
+           "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
            "FmhaError", "EXPORTED_SYMBOLS", "VARIANTS", "load_library"]
 
 
@@ -280,6 +281,49 @@ def merge_partials(o_part, lse_part, out=None, lse=None, return_lse: bool = True
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_merge_partials")
     return out, lse
+
+
+TRACE_EVENTS_PER_WAVE = 8192
+_PV_FORMATS = {"bf16": 0, "e4m3": 1, "e2m1": 2}
+
+
+def fwd_trace(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+              pv: str = "bf16", v_scale=None, softmax_scale: Optional[float] = None,
+              detailed: bool = False, traced_workgroups: int = 32) -> Tuple:
+    """Causal d=128 forward pass on the ping-pong kernel with a pipeline trace.
+
+    pv: "bf16" (v bf16), "e4m3" (v codes, v_scale fp32 [heads]) or "e2m1" (v MXFP4
+    codes, v_scale the E8M0 exponents). Returns (out, lse, trace) with trace
+    uint64 [traced_workgroups, 8, TRACE_EVENTS_PER_WAVE] on the device (see
+    head_attention_forward_fmha_amd.pipeline_trace for the records).
+    """
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, 3, dev)
+    _check_tensor("k", k, torch.bfloat16, 3, dev)
+    if pv not in _PV_FORMATS:
+        raise ValueError(f"pv must be one of {sorted(_PV_FORMATS)}")
+    _check_tensor("v", v, torch.bfloat16 if pv == "bf16" else torch.uint8, 3, dev)
+    if pv != "bf16":
+        _check_tensor("v_scale", v_scale, torch.float32 if pv == "e4m3" else torch.uint8,
+                      v_scale.dim(), dev)
+    s = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    trace = torch.zeros((int(traced_workgroups), 8, TRACE_EVENTS_PER_WAVE), dtype=torch.int64,
+                        device=dev)
+    st = lib.fmha_fwd_trace(_PV_FORMATS[pv], _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale),
+                            _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"], s["total_q"],
+                            s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"], 1,
+                            ctypes.c_float(scale), _ptr(out), _ptr(lse), int(bool(detailed)),
+                            int(traced_workgroups), _ptr(trace),
+                            trace.numel() * trace.element_size(),
+                            ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_fwd_trace")
+    return out, lse, trace
 
 
 def auto_variant(batch: int, max_seqlen_q: int, num_heads: int) -> str:

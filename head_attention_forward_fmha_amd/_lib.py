@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "fmha_fwd_splitkv_workspace_size",
     "fmha_fwd_splitkv_num_splits",
     "fmha_merge_partials",
+    "fmha_fwd_trace",
     "fmha_fwd_auto_variant",
     "fmha_validate_cu_seqlens",
     "fmha_status_string",
@@ -98,6 +99,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmha_fwd_splitkv_num_splits.restype = ctypes.c_int32
     lib.fmha_merge_partials.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.fmha_merge_partials.restype = ctypes.c_int
+    # pv_format, q, k, v, v_scale, cu_q, cu_k, 8 sizes/flags, scale, out, lse, detailed,
+    # traced workgroups, trace, trace bytes, stream
+    lib.fmha_fwd_trace.argtypes = ([_i32] + _FWD_FP8_ARGS[:-1] + [_i32, _i32, _vp, ctypes.c_size_t, _vp])
+    lib.fmha_fwd_trace.restype = ctypes.c_int
     lib.fmha_fwd_auto_variant.argtypes = [_i32, _i32, _i32]
     lib.fmha_fwd_auto_variant.restype = ctypes.c_int32
     lib.fmha_validate_cu_seqlens.argtypes = [_vp, _i32, _i32, _i32]

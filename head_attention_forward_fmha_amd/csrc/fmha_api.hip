@@ -11,6 +11,14 @@
 #include "fmha.h"
 #include "fmha_kernel_params.h"
 
+static_assert(FMHA_TRACE_EVENTS_PER_WAVE == fmha::kTraceEvents, "trace record count");
+static_assert(FMHA_TRACE_EV_SLOT == fmha::kEvSlot && FMHA_TRACE_EV_QK_DONE == fmha::kEvQkDone &&
+                  FMHA_TRACE_EV_MFMA_DONE == fmha::kEvMfmaDone &&
+                  FMHA_TRACE_EV_COPY_ISSUED == fmha::kEvCopyIssued &&
+                  FMHA_TRACE_EV_VALU_DONE == fmha::kEvValuDone &&
+                  FMHA_TRACE_EV_WAIT_DONE == fmha::kEvWaitDone && FMHA_TRACE_EV_ITEM == fmha::kEvItem,
+              "trace event codes");
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -257,6 +265,42 @@ fmha_status_t fmha_merge_partials(const float* o_part, const float* lse_part, in
     return FMHA_ERR_INVALID_ARG;
   hipError_t e = fmha::launch_merge_partials(o_part, lse_part, num_parts, total_q, num_heads,
                                              head_dim, out, lse, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+fmha_status_t fmha_fwd_trace(int32_t pv_format, const void* q, const void* k, const void* v,
+                             const void* v_scale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t total_q, int32_t total_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t num_heads, int32_t head_dim,
+                             int32_t causal, float softmax_scale,
+                             void* out, float* lse, int32_t detailed,
+                             int32_t traced_workgroups, uint64_t* trace, size_t trace_bytes,
+                             void* stream) {
+  if (pv_format < FMHA_PV_BF16 || pv_format > FMHA_PV_E2M1) return FMHA_ERR_INVALID_ARG;
+  fmha_status_t st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
+                                  softmax_scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (head_dim != 128 || causal != 1) return FMHA_ERR_UNSUPPORTED;
+  if (detailed != 0 && detailed != 1) return FMHA_ERR_INVALID_ARG;
+  if (pv_format != FMHA_PV_BF16 && total_k > 0 && v_scale == nullptr) return FMHA_ERR_INVALID_ARG;
+  if (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u)) return FMHA_ERR_INVALID_ARG;
+  if (traced_workgroups < 1 || traced_workgroups > 4096) return FMHA_ERR_INVALID_ARG;
+  const size_t need = (size_t)traced_workgroups * 8 * FMHA_TRACE_EVENTS_PER_WAVE * sizeof(uint64_t);
+  if (trace == nullptr || (reinterpret_cast<uintptr_t>(trace) & 7u) || trace_bytes < need)
+    return FMHA_ERR_INVALID_ARG;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
+  fmha::FwdParams p = make_params(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, softmax_scale, out, lse);
+  if (pv_format == FMHA_PV_E4M3) p.v_scale = static_cast<const float*>(v_scale);
+  if (pv_format == FMHA_PV_E2M1) p.v_mx_scale = static_cast<const uint8_t*>(v_scale);
+  p.trace = trace;
+  p.trace_wgs = traced_workgroups;
+  const int pv = pv_format == FMHA_PV_E4M3 ? fmha::kPvE4m3
+                 : pv_format == FMHA_PV_E2M1 ? fmha::kPvE2m1 : fmha::kPvBf16;
+  const hipError_t e = fmha::launch_fwd_trace(p, pv, true, detailed != 0, (hipStream_t)stream);
   return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
 

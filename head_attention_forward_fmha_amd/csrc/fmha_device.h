@@ -297,14 +297,12 @@ __device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f) {
   if constexpr (kPersistent) {
     ItemCursor cursor(n_work_items<kSplit>(params));
     int item;
-    bool first = true;
-    while (cursor.next(item)) {
-      // the previous item ended behind a barrier; this one keeps its epilogue
-      // apart from the next item's first copies
-      if (!first) __syncthreads();
-      first = false;
-      f(kernel_params(), item);
-    }
+    // Items follow each other without a workgroup barrier: every tile loop
+    // ends behind an LDS barrier (all reads of its stages done) and epilogues
+    // touch no LDS, so the next item's first copies cannot overwrite anything
+    // still read, and the previous item's output stores drain while the next
+    // item's loads are in flight.
+    while (cursor.next(item)) f(kernel_params(), item);
   } else {
     const int n_items = n_work_items<kSplit>(params);
     const int xcd = blockIdx.x % kXcds;
@@ -406,9 +404,9 @@ struct WaveTile {
       const bf16_t* qp = (const bf16_t*)p.q + (size_t)qrow * row_stride + w.head * kD + 8 * half;
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t) qreg[t] = *(const bf16x8*)(qp + 16 * t);
-      // Q has landed before the K/V stream starts, so no wait on the stream's
-      // vector-memory counter is ever needed for Q inside the tile loop
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      // The kernels wait for Q (vmcnt 0) before their tile loops, after issuing
+      // their first K/V copies, so the two HBM round trips overlap and no wait
+      // on the stream's counter is ever needed for Q inside the loop.
     }
 
     // operand read offsets. K rows 32*kb + col at logical chunk 2t + half.

@@ -80,6 +80,8 @@ void fmha_fwd_kernel(FwdParams params) {
   WT t;
   t.init(p, w, wave, wave);
   t.pin_copy_state();
+  // Q has landed before the K/V stream starts (its copies are counted by vmcnt)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * wave]);
   const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * wave]);
 
@@ -129,11 +131,47 @@ constexpr int kBM8 = kWaves8 * 32;  // query rows per workgroup
 static_assert(kBM8 == kRowsPingPong, "8-wave block height");
 constexpr int kStages8 = 3;         // K/V ring depth
 
-// Phase-boundary hooks for a coarse in-kernel timeline (s_memtime stamps). The
-// library instantiates the no-op version; a tracing build supplies its own.
+// Phase-boundary hooks of the ping-pong kernel. The forward entry points use
+// the no-op version; launch_fwd_trace uses StampTrace.
 struct NoPhaseTrace {
-  __device__ __forceinline__ void begin(int /*wave*/) {}
+  __device__ __forceinline__ void begin(const FwdParams& /*p*/, int /*wave*/) {}
   __device__ __forceinline__ void mark(int /*event*/) {}
+};
+
+// Pipeline timeline ("Kernel Bottleneck Tuning", section 2: trace the real
+// pipeline, coarsely). Each wave of the first p.trace_wgs workgroups records up
+// to kTraceEvents words (event << 56) | (s_memtime mod 2^56) from lane 0; the
+// waves of other workgroups start full and record nothing. A stamp (s_memtime)
+// is a side-effecting instruction the compiler cannot move work across, so every
+// stamp perturbs the schedule a little: the coarse mode keeps to slot and phase
+// ends; the detailed mode also splits the phases and lengthens them, and is for
+// locating time, not for measuring it.
+// The record pointer and count are held in vector registers (the empty asm
+// statements pin them there), leaving the kernel's scalar registers alone.
+template <bool kDetailed>
+struct StampTrace {
+  uint32_t out_lo, out_hi;
+  int idx;
+  __device__ __forceinline__ void begin(const FwdParams& p, int wave) {
+    const bool on = (int)blockIdx.x < p.trace_wgs;
+    const uint64_t o =
+        reinterpret_cast<uint64_t>(p.trace + ((size_t)blockIdx.x * kWaves8 + wave) * kTraceEvents);
+    out_lo = (uint32_t)o;
+    out_hi = (uint32_t)(o >> 32);
+    idx = on ? 0 : kTraceEvents;
+    asm volatile("" : "+v"(out_lo), "+v"(out_hi), "+v"(idx));
+  }
+  __device__ __forceinline__ void mark(int event) {
+    if (!kDetailed && (event == kEvQkDone || event == kEvCopyIssued || event == kEvWaitDone))
+      return;
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    if (idx < kTraceEvents && (threadIdx.x & 63) == 0) {
+      uint64_t* out = reinterpret_cast<uint64_t*>(((uint64_t)out_hi << 32) | out_lo);
+      out[idx] = ((uint64_t)event << 56) | (t & ((1ull << 56) - 1));
+    }
+    ++idx;
+    asm volatile("" : "+v"(idx));
+  }
 };
 
 template <int kD, bool kCausal, int kPv, bool kSplit, typename Trace = NoPhaseTrace>
@@ -146,7 +184,11 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   __shared__ __attribute__((aligned(1024))) char smem_k[kStages8][WT::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char smem_v[kStages8][WT::kVStageBytes];
 
+  Trace trace;
+  trace.begin(params, threadIdx.x >> 6);
+
   auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
+  trace.mark(kEvItem);
   int split = 0;
   if constexpr (kSplit) {
     split = item % p.num_splits;
@@ -169,8 +211,6 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   if constexpr (kCausal || WT::kFp4) t.pin_copy_state();
   const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * (wave & 3)]);
   const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * (wave & 3)]);
-  Trace trace;
-  trace.begin(wave);
 
   // Schedule. Tile j lives in stage j % 3. Slot 2j: group A runs the MFMA phase
   // of tile j (Q.K^T of tile j, P.V of tile j-1) while group B runs the VALU
@@ -187,10 +227,10 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
     constexpr int r = decltype(r_tag)::value;  // j % 3
     __builtin_amdgcn_s_setprio(2);
     if (j < n && t.active(j, causal_off)) t.qk(smem_k[r]);
-    trace.mark(1);
+    trace.mark(kEvQkDone);
     if (j >= 1 && t.active(j - 1, causal_off)) t.pv(smem_v[(r + 2) % 3]);
     __builtin_amdgcn_s_setprio(0);
-    trace.mark(2);
+    trace.mark(kEvMfmaDone);
   };
   auto valu_phase = [&](int j) {
     if (j >= 0 && j < n && t.active(j, causal_off)) t.softmax(j, w.sk, causal_off);
@@ -204,32 +244,32 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
     } else {
       const bool copy = j + 2 < n;
       if (copy) t.template copy_k<(r + 2) % 3>(j + 2, k_lds0);
-      trace.mark(3);
+      trace.mark(kEvCopyIssued);
       valu_phase(j - 1);
-      trace.mark(4);
+      trace.mark(kEvValuDone);
       // the copies of K tile j+1 (issued in slot 2j-2) have landed
       if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    trace.mark(5);
+    trace.mark(kEvWaitDone);
     lds_barrier();
-    trace.mark(0);
+    trace.mark(kEvSlot);
     // ---- slot 2j+1
     if (grp == 0) {
       const bool copy = j + 1 < n;
       if (copy) t.template copy_v<(r + 1) % 3>(j + 1, v_lds0);
-      trace.mark(3);
+      trace.mark(kEvCopyIssued);
       valu_phase(j);
-      trace.mark(4);
+      trace.mark(kEvValuDone);
       // the copies of V tile j (issued in slot 2j-1) have landed
       if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kVCopyOps));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     } else {
       mfma_phase(j, r_tag);
     }
-    trace.mark(5);
+    trace.mark(kEvWaitDone);
     lds_barrier();
-    trace.mark(0);
+    trace.mark(kEvSlot);
   };
 
   // prologue: K tiles 0 and 1 and V tile 0
@@ -239,8 +279,10 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   } else {
     if (n > 1) t.template copy_k<1>(1, k_lds0);
   }
+  // the first copies and Q (issued by init) have landed
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();
+  trace.mark(kEvSlot);
   int j = 0;
   for (; j + 3 <= n + 1; j += 3) {
     slot_pair(j, std::integral_constant<int, 0>());
@@ -289,6 +331,7 @@ void fmha_fwd_pipe_kernel(FwdParams params) {
   WT t;
   t.init(p, w, wave, wave);
   t.pin_copy_state();
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // Q has landed before the K/V stream starts
   t.alpha_o = 1.f;
   const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * wave]);
   const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * wave]);
@@ -444,6 +487,38 @@ hipError_t launch_fwd_fp4pv(const FwdParams& p, int head_dim, bool causal, int v
   if (head_dim != 128) return hipErrorInvalidValue;
   return causal ? launch<128, true, kPvE2m1>(p, variant, stream)
                 : launch<128, false, kPvE2m1>(p, variant, stream);
+}
+
+hipError_t launch_fwd_trace(const FwdParams& p, int pv, bool causal, bool detailed,
+                            hipStream_t stream) {
+  FwdParams q = p;
+  q.num_splits = 1;
+  q.n_mblocks = (p.max_seqlen_q + kBM8 - 1) / kBM8;
+  const long long n_items = (long long)q.n_mblocks * p.heads * p.batch;
+  if (n_items == 0) return hipSuccess;
+  if (n_items > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long grid = (std::min(n_items, (long long)device_cus()) + kXcds - 1) / kXcds * kXcds;
+  const dim3 g((unsigned)grid), b(kWaves8 * 64);
+#define FMHA_TRACE_LAUNCH(PV, CAUSAL)                                                              \
+  do {                                                                                             \
+    if (detailed)                                                                                  \
+      hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<128, CAUSAL, PV, false, StampTrace<true>>), g, b, \
+                         0, stream, q);                                                            \
+    else                                                                                           \
+      hipLaunchKernelGGL((fmha_fwd_pingpong_kernel<128, CAUSAL, PV, false, StampTrace<false>>), g, \
+                         b, 0, stream, q);                                                         \
+  } while (0)
+  if (!causal) return hipErrorInvalidValue;   // tracing covers the persistent (causal) launches
+  if (pv == kPvBf16)
+    FMHA_TRACE_LAUNCH(kPvBf16, true);
+  else if (pv == kPvE4m3)
+    FMHA_TRACE_LAUNCH(kPvE4m3, true);
+  else if (pv == kPvE2m1)
+    FMHA_TRACE_LAUNCH(kPvE2m1, true);
+  else
+    return hipErrorInvalidValue;
+#undef FMHA_TRACE_LAUNCH
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int head_dim, bool causal, int variant,

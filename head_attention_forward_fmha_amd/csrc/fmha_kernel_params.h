@@ -30,6 +30,26 @@ struct FwdParams {
   int32_t num_splits;     // 1 unless launched by launch_fwd_bf16_splitkv
   float* o_part;          // [num_splits, total_q, heads, d]
   float* lse_part;        // [num_splits, heads, total_q]
+  // pipeline tracing (launch_fwd_trace only): per traced wave, kTraceEvents
+  // 64-bit records (event << 56) | (shader clock counter mod 2^56)
+  uint64_t* trace;        // [trace_wgs, 8 waves, kTraceEvents]
+  int32_t trace_wgs;      // workgroups (lowest ids) that record
+};
+
+constexpr int kTraceEvents = 8192;   // records per traced wave; later events are dropped
+
+// Events of the ping-pong kernel's timeline (launch_fwd_trace). A slot is the
+// stretch between two workgroup barriers; in it a wave runs either the MFMA
+// phase (Q.K^T, then P.V) or the VALU phase (copies, mask and softmax, wait for
+// its copies).
+enum TraceEvent : int {
+  kEvSlot = 0,        // slot start (after the barrier)
+  kEvQkDone = 1,      // MFMA phase: Q.K^T issued (detailed mode)
+  kEvMfmaDone = 2,    // MFMA phase done
+  kEvCopyIssued = 3,  // VALU phase: copies issued (detailed mode)
+  kEvValuDone = 4,    // VALU phase: softmax done
+  kEvWaitDone = 5,    // before the barrier (detailed mode)
+  kEvItem = 6,        // a work item starts
 };
 
 // Number formats of the P.V product: bf16, fp8 e4m3 (one fp32 scale per head
@@ -75,6 +95,11 @@ hipError_t launch_fwd_bf16_splitkv(const FwdParams& p, int head_dim, bool causal
 hipError_t launch_merge_partials(const float* o_part, const float* lse_part, int num_parts,
                                  int total_q, int heads, int head_dim, void* out, float* lse,
                                  hipStream_t stream);
+// the causal ping-pong kernel (d = 128, P.V format pv) with phase stamps:
+// detailed stamps every event, coarse only kEvSlot, kEvMfmaDone, kEvValuDone,
+// kEvItem; p.trace_wgs workgroups record into p.trace
+hipError_t launch_fwd_trace(const FwdParams& p, int pv, bool causal, bool detailed,
+                            hipStream_t stream);
 // split count the automatic choice uses for a problem on the current device
 int recommended_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                        int32_t heads, bool causal, int variant);

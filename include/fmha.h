@@ -247,6 +247,54 @@ fmha_status_t fmha_merge_partials(const float* o_part, const float* lse_part, in
                                   void* out, float* lse, void* stream);
 
 /*
+ * Pipeline trace of the forward pass ("Kernel Bottleneck Tuning (validated on
+ * FA4 FP4/FP8 PV, GB300)", section 2: trace the real pipeline, coarsely). Runs
+ * the causal 8-wave ping-pong kernel on the problem, computing out and lse as
+ * the forward entry points do, while every wave of the first
+ * traced_workgroups workgroups records its phase boundaries:
+ *   trace[wg][wave][i], wg < traced_workgroups, wave < 8, i < FMHA_TRACE_EVENTS_PER_WAVE:
+ *     (event << 56) | (shader clock counter mod 2^56), from s_memtime.
+ * Records after a wave's FMHA_TRACE_EVENTS_PER_WAVE-th are dropped; entries it
+ * did not write keep their contents, so clear the buffer first (a zero word
+ * ends a wave's records). Events (FMHA_TRACE_EV_*): a slot is the stretch
+ * between two workgroup barriers, in which a wave runs either the MFMA phase
+ * (Q.K^T, then P.V) or the VALU phase (copies, mask and softmax, wait for its
+ * copies); ITEM marks the start of each work item. detailed = 0 (coarse)
+ * records SLOT, MFMA_DONE, VALU_DONE and ITEM; detailed = 1 all of them.
+ * Each stamp is a side-effecting scalar instruction that the compiler cannot
+ * schedule work across: the coarse mode perturbs the pipeline least; detailed
+ * spans are longer than the untraced kernel's and locate time rather than
+ * measure it.
+ *   pv_format  FMHA_PV_BF16 (v bf16, v_scale NULL), FMHA_PV_E4M3 (v e4m3 codes,
+ *              v_scale fp32 [heads]) or FMHA_PV_E2M1 (v MXFP4 codes, v_scale the
+ *              E8M0 exponents), as fmha_fwd / _fp8pv / _fp4pv
+ *   causal     must be 1; head_dim must be 128 (else FMHA_ERR_UNSUPPORTED)
+ *   trace      8-byte aligned, at least traced_workgroups * 8 *
+ *              FMHA_TRACE_EVENTS_PER_WAVE * 8 bytes; traced_workgroups 1..4096
+ */
+#define FMHA_PV_BF16 0
+#define FMHA_PV_E4M3 1
+#define FMHA_PV_E2M1 2
+#define FMHA_TRACE_EVENTS_PER_WAVE 8192
+#define FMHA_TRACE_EV_SLOT 0         /* slot start, after the barrier          */
+#define FMHA_TRACE_EV_QK_DONE 1      /* MFMA phase: Q.K^T issued (detailed)     */
+#define FMHA_TRACE_EV_MFMA_DONE 2    /* MFMA phase done                         */
+#define FMHA_TRACE_EV_COPY_ISSUED 3  /* VALU phase: copies issued (detailed)    */
+#define FMHA_TRACE_EV_VALU_DONE 4    /* VALU phase: softmax done                */
+#define FMHA_TRACE_EV_WAIT_DONE 5    /* copies landed, before the barrier (detailed) */
+#define FMHA_TRACE_EV_ITEM 6         /* a work item starts                      */
+fmha_status_t fmha_fwd_trace(int32_t pv_format, const void* q, const void* k, const void* v,
+                             const void* v_scale,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t total_q, int32_t total_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int32_t num_heads, int32_t head_dim,
+                             int32_t causal, float softmax_scale,
+                             void* out, float* lse, int32_t detailed,
+                             int32_t traced_workgroups, uint64_t* trace, size_t trace_bytes,
+                             void* stream);
+
+/*
  * The kernel variant FMHA_VARIANT_AUTO resolves to for a problem of `batch`
  * documents, longest query document max_seqlen_q and num_heads heads:
  * FMHA_VARIANT_FOUR_WAVE or FMHA_VARIANT_PINGPONG. Negative sizes give -1.
@@ -268,7 +316,7 @@ const char* fmha_status_string(fmha_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int32_t fmha_abi_version(void);
 
-#define FMHA_ABI_VERSION ((1 << 16) | 2)
+#define FMHA_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

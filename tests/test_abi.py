@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     assert names == sorted(["fmha_fwd", "fmha_fwd_fp8pv", "fmha_fwd_variant",
                             "fmha_fwd_fp8pv_variant", "fmha_fwd_fp4pv", "fmha_fwd_fp4pv_variant",
                             "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size",
-                            "fmha_fwd_splitkv_num_splits", "fmha_merge_partials",
+                            "fmha_fwd_splitkv_num_splits", "fmha_merge_partials", "fmha_fwd_trace",
                             "fmha_fwd_auto_variant", "fmha_validate_cu_seqlens",
                             "fmha_status_string", "fmha_abi_version"])
 
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert set(fm.EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert fm.abi_version() == (1 << 16) | 2
+    assert fm.abi_version() == (1 << 16) | 3
 
 
 def test_status_strings():
@@ -191,6 +191,28 @@ def test_splitkv_argument_checks():
     a = list(margs)
     a[3] = 0
     assert lib.fmha_merge_partials(*a) == 0
+
+
+def test_trace_argument_checks():
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    need = 2 * 8 * fm.TRACE_EVENTS_PER_WAVE * 8
+    # pv, q, k, v, v_scale, cu_q, cu_k, batch, tq, tk, mq, mk, heads, d, causal, scale, out, lse
+    base = [0, 0x10000, 0x20000, 0x30000, None, None, None, 1, 256, 256, 256, 256, 2, 128, 1,
+            ctypes.c_float(0.088), 0x40000, 0x50000]
+    # every call below has one bad argument: the checks return before any launch
+    tail = [0, 2, 0x80000, need, None]              # detailed, workgroups, trace, bytes, stream
+    for i, bad, status in ((0, 3, 1), (13, 64, 2), (14, 0, 2), (4, 0x70002, 1)):
+        b = list(base)
+        b[i] = bad
+        assert lib.fmha_fwd_trace(*b, *tail) == status, (i, bad)
+    b = list(base)
+    b[0] = 1                                         # e4m3 needs its per-head scales
+    assert lib.fmha_fwd_trace(*b, *tail) == 1
+    for i, bad in ((0, 2), (1, 0), (1, 4097), (2, None), (2, 0x80004), (3, need - 1)):
+        t = list(tail)
+        t[i] = bad
+        assert lib.fmha_fwd_trace(*base, *t) == 1, (i, bad)
 
 
 def test_splitkv_num_splits_choice():
