@@ -22,6 +22,9 @@ Parity status per function:
   merge_partials -- pinned (attention over disjoint key ranges, each taken
       with the oracle's own masked softmax, merges to attention over all keys;
       empty ranges and empty rows).
+  attention_backward -- pinned (central finite differences of the forward
+      oracle, invariants of the definition, torch float64 autograd);
+  loss_grad_mean_square -- pinned (torch autograd of mean(O^2)).
 """
 
 from .reference import (DEFAULT_ROW_BLOCK, attention, attention_bruteforce, attention_rows,
@@ -29,6 +32,7 @@ from .reference import (DEFAULT_ROW_BLOCK, attention, attention_bruteforce, atte
 from .fp8 import (E4M3_MAX, attention_fp8pv, attention_fp8pv_emulated, attention_fp8pv_sampled,
                   dequantize_v, e4m3_decode, e4m3_encode)
 from .merge import merge_partials
+from .backward import attention_backward, loss_grad_mean_square
 from .fp4 import (E2M1_MAX, FP4Emulation, attention_fp4pv, attention_fp4pv_bruteforce,
                   attention_fp4pv_emulated, attention_fp4pv_sampled, e2m1_decode, e2m1_encode,
                   mx_dequantize_v)
@@ -39,5 +43,5 @@ __all__ = [
     "attention_fp8pv_emulated", "attention_fp8pv_sampled", "dequantize_v", "e4m3_decode",
     "e4m3_encode", "E2M1_MAX", "FP4Emulation", "attention_fp4pv", "attention_fp4pv_bruteforce",
     "attention_fp4pv_emulated", "attention_fp4pv_sampled", "e2m1_decode", "e2m1_encode",
-    "mx_dequantize_v", "merge_partials",
+    "mx_dequantize_v", "merge_partials", "attention_backward", "loss_grad_mean_square",
 ]
