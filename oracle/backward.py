@@ -28,6 +28,23 @@ oracle's sum(dO * O), invariants of the definition (the key gradients of a row
 sum to zero, sum_j dV_j = sum_i dO_i over rows that see a key, constant V gives
 dQ = dK = 0, a shift of all keys by one vector changes no gradient) and torch
 float64 autograd through a plainly written dense attention.
+
+Rounding scale (``rounding_scale=True``). The pages fix no precision for the
+backward; the reading taken is the forward's: bf16 operands of every matrix
+product, fp32 accumulation. A gradient element is then a sum whose terms carry
+one bf16 rounding each (relative at most 2^-9): P's in dV_jd = sum_i P_ij dO_id,
+dS's in dQ and dK, and the row value D_i = dO_i . O_i taken from a bf16 O, whose
+error moves every dS_ij of row i by -P_ij dD_i. The scale returned per element
+is the root sum of squares of those worst-case term errors,
+
+  T(dV_jd) = 2^-9 sqrt(sum_i P_ij^2 dO_id^2)
+  T(dQ_id) = tau sqrt(2^-18 sum_j dS_ij^2 K_jd^2 + e_i^2 (P K)_id^2)
+  T(dK_jd) = tau sqrt(2^-18 sum_i dS_ij^2 Q_id^2 + sum_i P_ij^2 e_i^2 Q_id^2)
+
+with e_i = sqrt(sum_d dO_id^2 o_id^2) and o_id = 2^-9 (|O_id| + sqrt(sum_j
+P_ij^2 V_jd^2)) the size of O's own error (its final rounding and the bf16 P of
+the forward's P.V). Independent unbiased roundings sum to an error of that
+order; a parity bar is a multiple of it (plus the output's own rounding).
 """
 
 from __future__ import annotations
@@ -49,12 +66,21 @@ def loss_grad_mean_square(o) -> np.ndarray:
     return 2.0 * of / of.size
 
 
-def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block):
-    """Gradients for one (document, head): q/do [sq, d], k/v [sk, d] in fp64."""
+_U = 2.0 ** -9   # unit roundoff of bf16 (round to nearest)
+
+
+def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block, want_scale=False):
+    """Gradients for one (document, head): q/do [sq, d], k/v [sk, d] in fp64.
+
+    With want_scale, also the rounding scales T(dQ), T(dK), T(dV) (module
+    docstring); their squares are accumulated over row blocks."""
     sk = kb.shape[0]
     dq = np.zeros_like(qb)
     dk = np.zeros_like(kb)
     dv = np.zeros_like(vb)
+    t2q = np.zeros_like(qb)
+    t2k = np.zeros_like(kb)
+    t2v = np.zeros_like(vb)
     for r0 in range(0, sq, row_block):
         r1 = min(sq, r0 + row_block)
         rows = np.arange(r0, r1)
@@ -65,25 +91,35 @@ def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block):
         dv += p.T @ dob[r0:r1]
         dq[r0:r1] = tau * (ds @ kb)
         dk += tau * (ds.T @ qb[r0:r1])
+        if want_scale:
+            p2, ds2 = p * p, ds * ds
+            o = p @ vb
+            o_err = _U * (np.abs(o) + np.sqrt(p2 @ (vb * vb)))
+            e2 = ((dob[r0:r1] * o_err) ** 2).sum(axis=1)          # e_i^2
+            q2 = qb[r0:r1] ** 2
+            t2v += _U * _U * (p2.T @ (dob[r0:r1] ** 2))
+            t2q[r0:r1] = tau * tau * (_U * _U * (ds2 @ (kb * kb)) + e2[:, None] * (p @ kb) ** 2)
+            t2k += tau * tau * (_U * _U * (ds2.T @ q2) + (p2 * e2[:, None]).T @ q2)
+    if want_scale:
+        return dq, dk, dv, np.sqrt(t2q), np.sqrt(t2k), np.sqrt(t2v)
     return dq, dk, dv
 
 
 def attention_backward(q, k, v, dout, cu_seqlens_q: Sequence[int], cu_seqlens_k: Sequence[int],
                        causal: bool, softmax_scale: float, row_block: int = DEFAULT_ROW_BLOCK,
                        heads: Optional[Iterable[int]] = None,
-                       docs: Optional[Iterable[int]] = None):
+                       docs: Optional[Iterable[int]] = None, rounding_scale: bool = False):
     """Gradients of packed varlen attention.
 
     q, dout [total_q, h, d]; k, v [total_k, h, d]; any float dtype (widened
-    exactly to fp64). Returns (dQ, dK, dV) fp64 in the shapes of q, k, v. Rows
-    of documents or heads not selected (``heads``/``docs``) are NaN.
+    exactly to fp64). Returns (dQ, dK, dV) fp64 in the shapes of q, k, v, and
+    with ``rounding_scale`` also their rounding scales (T(dQ), T(dK), T(dV)).
+    Rows of documents or heads not selected (``heads``/``docs``) are NaN.
     """
     cq = np.asarray(cu_seqlens_q, dtype=np.int64)
     ck = np.asarray(cu_seqlens_k, dtype=np.int64)
     tau = float(np.float32(softmax_scale))
-    dq = np.full(q.shape, np.nan)
-    dk = np.full(k.shape, np.nan)
-    dv = np.full(v.shape, np.nan)
+    outs = [np.full(x.shape, np.nan) for x in (q, k, v) * (2 if rounding_scale else 1)]
     head_list = range(q.shape[1]) if heads is None else list(heads)
     doc_list = range(len(cq) - 1) if docs is None else list(docs)
     for b in doc_list:
@@ -91,6 +127,10 @@ def attention_backward(q, k, v, dout, cu_seqlens_q: Sequence[int], cu_seqlens_k:
         for hh in head_list:
             g = _backward_one(_as_f64(q[q0:q1, hh, :]), _as_f64(k[k0:k1, hh, :]),
                               _as_f64(v[k0:k1, hh, :]), _as_f64(dout[q0:q1, hh, :]),
-                              q1 - q0, causal, tau, row_block)
-            dq[q0:q1, hh, :], dk[k0:k1, hh, :], dv[k0:k1, hh, :] = g
-    return dq, dk, dv
+                              q1 - q0, causal, tau, row_block, rounding_scale)
+            for n, x in enumerate(g):
+                rows = slice(q0, q1) if n % 3 == 0 else slice(k0, k1)
+                outs[n][rows, hh, :] = x
+    if rounding_scale:
+        return tuple(outs[:3]), tuple(outs[3:])
+    return tuple(outs)

@@ -9,6 +9,9 @@
   that see a key; O does not depend on Q or K when V is constant, nor on a shift
   of all keys by one vector; the gradients are linear in dO.
 * torch float64 autograd through a plainly written dense attention.
+* The rounding scale (the parity bar's unit) against an emulation of the bf16
+  operand roundings it models, which it must cover, and a planted masking
+  mistake, which must exceed the bar.
 """
 
 import numpy as np
@@ -132,3 +135,54 @@ def test_mean_square_loss_gradient():
     o.square().mean().backward()
     np.testing.assert_allclose(oracle.loss_grad_mean_square(o.detach()), o.grad.numpy(),
                                atol=1e-15)
+
+
+def _bf16(x):
+    return (torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+            .astype(np.float64))
+
+
+def _emulated_bf16_backward(q, k, v, do, cu_q, cu_k, causal, tau, drop_key=None):
+    """The backward with the roundings the rounding scale models: the forward's O
+    from a bf16 P and rounded to bf16, D from that O, P and dS rounded to bf16 as
+    operands, outputs rounded to bf16. drop_key=(doc, j) hides key j of that
+    document from every row (a planted masking mistake)."""
+    out = [np.zeros_like(x) for x in (q, k, v)]
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        sq, sk = q1 - q0, k1 - k0
+        vis = oracle.visible(np.arange(sq), sq, sk, causal)
+        if drop_key is not None and drop_key[0] == b:
+            vis = vis.copy()
+            vis[:, drop_key[1]] = False
+        for h in range(q.shape[1]):
+            p, _, _ = oracle.softmax_rows(tau * q[q0:q1, h] @ k[k0:k1, h].T, vis)
+            o = _bf16(_bf16(p) @ v[k0:k1, h])
+            dp = do[q0:q1, h] @ v[k0:k1, h].T
+            dsb = _bf16(p * (dp - (do[q0:q1, h] * o).sum(1)[:, None]))
+            out[0][q0:q1, h] = _bf16(tau * dsb @ k[k0:k1, h])
+            out[1][k0:k1, h] = _bf16(tau * dsb.T @ q[q0:q1, h])
+            out[2][k0:k1, h] = _bf16(_bf16(p).T @ do[q0:q1, h])
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rounding_scale_covers_bf16_operands(causal):
+    """The rounding scale bounds the error of bf16 operands: an emulation of those
+    roundings stays within 6 T + 2^-8 |g| (the GPU bar is 8 T + 2^-8 |g|), and a
+    planted mistake (one key hidden from every row) does not."""
+    lens = ((200, 200), (70, 150), (129, 129))
+    q, k, v, do, cu_q, cu_k = _tiny(lens, 2, 64, seed=11)
+    q, k, v, do = (_bf16(x) for x in (q, k, v, do))
+    tau = float(np.float32(1 / 8))
+    ref, scale = oracle.attention_backward(q, k, v, do, cu_q, cu_k, causal, tau,
+                                           rounding_scale=True)
+    emu = _emulated_bf16_backward(q, k, v, do, cu_q, cu_k, causal, tau)
+    for e, r, t in zip(emu, ref, scale):
+        assert np.all(np.abs(e - r) <= 6 * t + 2.0 ** -8 * np.abs(r))
+    bad = _emulated_bf16_backward(q, k, v, do, cu_q, cu_k, causal, tau, drop_key=(0, 37))
+    assert any(np.any(np.abs(e - r) > 8 * t + 2.0 ** -8 * np.abs(r))
+               for e, r, t in zip(bad, ref, scale))
+    # the scale is a small fraction of the gradients' size, not a blanket allowance
+    for r, t in zip(ref, scale):
+        assert np.median(t) < 5e-3 * np.sqrt(np.mean(r * r))
