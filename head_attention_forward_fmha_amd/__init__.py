@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import FMHA_OK, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "fwd_splitkv", "splitkv_num_splits",
+__all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "bwd", "bwd_workspace_size", "fwd_splitkv", "splitkv_num_splits",
            "splitkv_workspace_size", "merge_partials", "fwd_trace", "TRACE_EVENTS_PER_WAVE",
            "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
            "FmhaError", "EXPORTED_SYMBOLS", "VARIANTS", "load_library"]
@@ -259,6 +259,57 @@ def fwd_splitkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None,
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_fwd_splitkv")
     return out, lse
+
+
+def bwd_workspace_size(total_q: int, num_heads: int) -> int:
+    """Bytes of device workspace fmha_bwd needs (D and LSE*log2(e) per row and head)."""
+    return int(_lib.load().fmha_bwd_workspace_size(int(total_q), int(num_heads)))
+
+
+def bwd(q, k, v, out, dout, lse, cu_seqlens_q=None, cu_seqlens_k=None,
+        max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+        causal: bool = False, softmax_scale: Optional[float] = None, dq=None, dk=None, dv=None,
+        workspace=None) -> Tuple:
+    """Backward pass of ``fwd``: (dq, dk, dv) bf16 given the forward's inputs, its output
+    ``out``, its natural-log ``lse`` [h, total_q] and the upstream gradient ``dout``.
+    ``workspace`` (allocated when None) is a device tensor of at least
+    bwd_workspace_size(total_q, heads) bytes."""
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    for name, t, ref in (("q", q, q), ("k", k, q), ("v", v, q), ("out", out, q),
+                         ("dout", dout, q)):
+        _check_tensor(name, t, torch.bfloat16, ref.dim(), dev)
+    s = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if k.shape != v.shape or k.shape[-2:] != q.shape[-2:]:
+        raise ValueError("k and v must match, with q's heads and head_dim")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    _check_tensor("lse", lse, torch.float32, 2, dev)
+    if tuple(lse.shape) != (s["heads"], s["lse_len"]):
+        raise ValueError("lse must be [heads, total_q]")
+    scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
+    need = bwd_workspace_size(s["total_q"], s["heads"])
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, torch.bfloat16, ref.dim(), dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have the shape of its input")
+    st = lib.fmha_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                      _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"], s["total_q"], s["total_k"],
+                      s["max_q"], s["max_k"], s["heads"], s["d"], int(bool(causal)),
+                      ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                      ws_bytes, ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_bwd")
+    return dq, dk, dv
 
 
 def merge_partials(o_part, lse_part, out=None, lse=None, return_lse: bool = True) -> Tuple:

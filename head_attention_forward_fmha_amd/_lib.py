@@ -32,6 +32,8 @@ EXPORTED_SYMBOLS = (
     "fmha_fwd_splitkv_num_splits",
     "fmha_merge_partials",
     "fmha_fwd_trace",
+    "fmha_bwd",
+    "fmha_bwd_workspace_size",
     "fmha_fwd_auto_variant",
     "fmha_validate_cu_seqlens",
     "fmha_status_string",
@@ -103,6 +105,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     # traced workgroups, trace, trace bytes, stream
     lib.fmha_fwd_trace.argtypes = ([_i32] + _FWD_FP8_ARGS[:-1] + [_i32, _i32, _vp, ctypes.c_size_t, _vp])
     lib.fmha_fwd_trace.restype = ctypes.c_int
+    lib.fmha_bwd.argtypes = ([_vp] * 8 + [_i32] * 8 + [_f32] + [_vp] * 4 +
+                             [ctypes.c_size_t, _vp])
+    lib.fmha_bwd.restype = ctypes.c_int
+    lib.fmha_bwd_workspace_size.argtypes = [_i32, _i32]
+    lib.fmha_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fmha_fwd_auto_variant.argtypes = [_i32, _i32, _i32]
     lib.fmha_fwd_auto_variant.restype = ctypes.c_int32
     lib.fmha_validate_cu_seqlens.argtypes = [_vp, _i32, _i32, _i32]

@@ -25,7 +25,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfmha.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 RESOURCE_REPORT = os.path.join(PKG_DIR, "libfmha.resource-usage.txt")
-SOURCES = ["fmha_fwd_kernel.hip", "fmha_merge.hip", "fmha_api.hip"]
+SOURCES = ["fmha_fwd_kernel.hip", "fmha_merge.hip", "fmha_bwd_kernel.hip", "fmha_api.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

@@ -251,6 +251,62 @@ fmha_status_t fmha_fwd_splitkv(const void* q, const void* k, const void* v,
   return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
 }
 
+size_t fmha_bwd_workspace_size(int32_t total_q, int32_t num_heads) {
+  if (total_q < 0 || num_heads <= 0) return 0;
+  return 2 * (size_t)total_q * (size_t)num_heads * sizeof(float);
+}
+
+fmha_status_t fmha_bwd(const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* lse,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int32_t batch, int32_t total_q, int32_t total_k,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t num_heads, int32_t head_dim,
+                       int32_t causal, float softmax_scale,
+                       void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  fmha_status_t st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                                  max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
+                                  softmax_scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (total_q > 0 && (dout == nullptr || lse == nullptr || dq == nullptr))
+    return FMHA_ERR_INVALID_ARG;
+  if (total_k > 0 && (dk == nullptr || dv == nullptr)) return FMHA_ERR_INVALID_ARG;
+  if ((dout && !aligned16(dout)) || (dq && !aligned16(dq)) || (dk && !aligned16(dk)) ||
+      (dv && !aligned16(dv)))
+    return FMHA_ERR_INVALID_ARG;
+  if (((int64_t)max_seqlen_k + 127) / 128 * num_heads * batch > INT32_MAX)
+    return FMHA_ERR_UNSUPPORTED;
+  const size_t need = fmha_bwd_workspace_size(total_q, num_heads);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return FMHA_ERR_INVALID_ARG;
+  if (batch == 0 || (total_q == 0 && total_k == 0)) return FMHA_OK;
+  fmha::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = static_cast<float*>(workspace);
+  p.lse2 = p.delta + (size_t)total_q * num_heads;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.max_seqlen_q = max_seqlen_q;
+  p.max_seqlen_k = max_seqlen_k;
+  p.heads = num_heads;
+  p.scale = softmax_scale;
+  p.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = fmha::launch_bwd(p, head_dim, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
 fmha_status_t fmha_merge_partials(const float* o_part, const float* lse_part, int32_t num_parts,
                                   int32_t total_q, int32_t num_heads, int32_t head_dim,
                                   void* out, float* lse, void* stream) {

@@ -295,6 +295,46 @@ fmha_status_t fmha_fwd_trace(int32_t pv_format, const void* q, const void* k, co
                              void* stream);
 
 /*
+ * Backward pass of fmha_fwd: dQ, dK, dV of the attention given the upstream
+ * gradient dO, with P recomputed from the forward's LSE. The step timed in
+ * "CuTe DSL 4.7/4.8 regression: FlashAttention-4 SM100 forward kernel spills
+ * registers" (Describe the bug; Steps/Code to reproduce bug) is that forward
+ * followed by this backward of mean(O^2). For every document and head, with
+ * P as defined at the top of this header and tau = softmax_scale:
+ *
+ *     dV = P^T dO,  dP = dO V^T,  dS_ij = P_ij (dP_ij - D_i),  D_i = dO_i . O_i,
+ *     dQ = tau dS K,  dK = tau dS^T Q,
+ *
+ * (D_i = sum_j P_ij dP_ij, as O_i = sum_j P_ij V_j). Query rows that saw no key
+ * (LSE = -inf) contribute nothing and get dQ = 0; keys no query sees get
+ * dK = dV = 0. The result is deterministic: every element is summed in a fixed
+ * order, without atomics. P and dS are rounded to bf16 as MFMA operands, D is
+ * taken from the bf16 O, accumulation is fp32.
+ *   q, k, v, cu_seqlens_*, sizes, causal, softmax_scale   as for fmha_fwd
+ *   out       bf16 [total_q, num_heads, head_dim], the forward's output
+ *   dout      bf16 [total_q, num_heads, head_dim], 16-byte aligned
+ *   lse       fp32 [num_heads, total_q], the forward's LSE (required)
+ *   dq        bf16 [total_q, num_heads, head_dim], 16-byte aligned
+ *   dk, dv    bf16 [total_k, num_heads, head_dim], 16-byte aligned
+ *   workspace device memory of at least fmha_bwd_workspace_size(total_q,
+ *             num_heads) bytes, 16-byte aligned, owned by the caller; it holds
+ *             D and LSE * log2(e) per (head, row) and may be reused once the
+ *             stream has passed this call
+ * Errors as for fmha_fwd; a missing or short workspace, or a NULL dout, lse,
+ * dq, dk or dv for a non-empty problem, gives FMHA_ERR_INVALID_ARG.
+ */
+size_t fmha_bwd_workspace_size(int32_t total_q, int32_t num_heads);
+fmha_status_t fmha_bwd(const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* lse,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int32_t batch, int32_t total_q, int32_t total_k,
+                       int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t num_heads, int32_t head_dim,
+                       int32_t causal, float softmax_scale,
+                       void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The kernel variant FMHA_VARIANT_AUTO resolves to for a problem of `batch`
  * documents, longest query document max_seqlen_q and num_heads heads:
  * FMHA_VARIANT_FOUR_WAVE or FMHA_VARIANT_PINGPONG. Negative sizes give -1.
@@ -316,7 +356,7 @@ const char* fmha_status_string(fmha_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int32_t fmha_abi_version(void);
 
-#define FMHA_ABI_VERSION ((1 << 16) | 3)
+#define FMHA_ABI_VERSION ((1 << 16) | 4)
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,10 @@ exponent X = floor(log2(max|V|)) - 2 (the MX rule for e2m1, whose largest
 exponent is 2; -127 for an all-zero block), and e2m1 codes of V / 2^X rounded
 to nearest, ties to even, saturating at 6. Codes are packed two per byte along
 d (even d in the low nibble); exponents are stored as X + 127.
+
+The backward pass takes an upstream gradient dO of q's shape: a standard-normal
+draw rounded to bf16 from its own generator, seeded with seed + 1, so that it is
+independent of q, k and v (``make_dout``).
 """
 
 from __future__ import annotations
@@ -236,6 +240,12 @@ def make_inputs(lens, heads: int, head_dim: int, seed: int = 0, fp8_pv: bool = F
     if fp4_pv:
         inp.v_e2m1, inp.v_mx_scale = quantize_v_mxfp4(v)
     return inp
+
+
+def make_dout(total_q: int, heads: int, head_dim: int, seed: int = 0) -> torch.Tensor:
+    """Upstream gradient dO [total_q, heads, head_dim] bf16, N(0, 1), seeded with seed + 1."""
+    gen = torch.Generator().manual_seed(int(seed) + 1)
+    return randn_bf16((total_q, heads, head_dim), gen)
 
 
 def workload_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:

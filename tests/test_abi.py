@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
                             "fmha_fwd_fp8pv_variant", "fmha_fwd_fp4pv", "fmha_fwd_fp4pv_variant",
                             "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size",
                             "fmha_fwd_splitkv_num_splits", "fmha_merge_partials", "fmha_fwd_trace",
-                            "fmha_fwd_auto_variant", "fmha_validate_cu_seqlens",
+                            "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_auto_variant", "fmha_validate_cu_seqlens",
                             "fmha_status_string", "fmha_abi_version"])
 
 
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert set(fm.EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert fm.abi_version() == (1 << 16) | 3
+    assert fm.abi_version() == (1 << 16) | 4
 
 
 def test_status_strings():
@@ -213,6 +213,30 @@ def test_trace_argument_checks():
         t = list(tail)
         t[i] = bad
         assert lib.fmha_fwd_trace(*base, *t) == 1, (i, bad)
+
+
+def test_bwd_argument_checks():
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    assert lib.fmha_bwd_workspace_size(300, 4) == 2 * 300 * 4 * 4
+    assert lib.fmha_bwd_workspace_size(-1, 4) == 0 and lib.fmha_bwd_workspace_size(3, 0) == 0
+    need = 2 * 256 * 2 * 4
+    # q, k, v, out, dout, lse, cu_q, cu_k, batch, tq, tk, mq, mk, heads, d, causal, scale,
+    # dq, dk, dv, workspace, bytes, stream
+    base = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, None, None, 1, 256, 256,
+            256, 256, 2, 128, 1, ctypes.c_float(0.088), 0x70000, 0x80000, 0x90000, 0xa0000,
+            need, None]
+    # every call below has one bad argument: the checks return before any launch
+    for i, bad, status in ((4, None, 1), (5, None, 1), (17, None, 1), (18, None, 1),
+                           (19, None, 1), (4, 0x50008, 1), (17, 0x70002, 1), (19, 0x90004, 1),
+                           (20, None, 1), (20, 0xa0008, 1), (21, need - 1, 1), (14, 96, 2),
+                           (15, 2, 1), (16, ctypes.c_float(0.0), 1), (9, 255, 1)):
+        b = list(base)
+        b[i] = bad
+        assert lib.fmha_bwd(*b) == status, (i, bad)
+    # nothing to compute: no launch
+    empty = [None] * 8 + [0, 0, 0, 0, 0, 2, 64, 0, ctypes.c_float(0.125)] + [None] * 4 + [0, None]
+    assert lib.fmha_bwd(*empty) == 0
 
 
 def test_splitkv_num_splits_choice():

@@ -1,0 +1,210 @@
+"""GPU parity of the backward pass (fmha_bwd) against the fp64 oracle.
+
+Bar. The pages fix no precision for the backward; the reading taken is the
+forward's arithmetic, bf16 operands of every matrix product with fp32
+accumulation. Each gradient element is a sum whose terms carry one bf16
+rounding each (P in dV, dS in dQ and dK, and D = dO . O taken from the bf16 O),
+so its error is of the order of the oracle's rounding scale T (the root sum of
+squares of those terms' worst-case rounding errors; see oracle/backward.py).
+An element g passes when
+
+    |g - g_ref| <= 8 T + 2^-8 |g_ref|,
+
+2^-8 |g_ref| covering the output's own rounding to bf16. An emulation of these
+roundings stays within 6 T on the CPU (tests/test_oracle_backward.py), and T is
+about 0.1 % of a gradient's rms, so a masking or indexing mistake fails.
+
+Inputs. Two paths: (a) the step's own path, the library's forward followed by
+its backward, and (b) the backward alone given the oracle's O (rounded to bf16)
+and LSE (rounded to fp32), which isolates the backward kernels. dO is an
+independent N(0, 1) bf16 draw, or the gradient of mean(O^2) taken from the
+oracle's O. Every expected value comes from the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic import WORKLOADS, make_dout, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+K_SCALE = 8.0      # multiple of the rounding scale
+RTOL = 2.0 ** -8  # the output's own bf16 rounding
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _cu(x, dev):
+    return torch.from_numpy(np.asarray(x, np.int32)).to(dev)
+
+
+def _gpu_bwd(inp, dout, causal, scale, out=None, lse=None):
+    """The library's forward (unless out/lse are given) and backward; fp64 numpy grads."""
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq, ck = _cu(inp.cu_q, dev), _cu(inp.cu_k, dev)
+    mq = int(np.diff(inp.cu_q).max()) if len(inp.cu_q) > 1 else 0
+    mk = int(np.diff(inp.cu_k).max()) if len(inp.cu_k) > 1 else 0
+    if out is None:
+        out, lse = fm.fwd(q, k, v, cq, ck, mq, mk, causal=causal, softmax_scale=scale)
+    else:
+        out, lse = out.to(dev), lse.to(dev)
+    nan = float("nan")
+    dq = torch.full_like(q, nan)
+    dk = torch.full_like(k, nan)
+    dv = torch.full_like(v, nan)
+    fm.bwd(q, k, v, out, dout.to(dev), lse, cq, ck, mq, mk, causal=causal, softmax_scale=scale,
+           dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+
+
+def _check(got, ref, scale, what):
+    for name, g, r, t in zip(("dQ", "dK", "dV"), got, ref, scale):
+        assert not np.isnan(g).any(), f"{what}: NaN in {name} (unwritten or invalid)"
+        if r.size == 0:
+            continue
+        err = np.abs(g - r)
+        tol = K_SCALE * t + RTOL * np.abs(r)
+        bad = err > tol
+        if bad.any():
+            i = np.unravel_index(np.argmax(err / np.maximum(tol, 1e-300)), err.shape)
+            raise AssertionError(f"{what}: {name} {bad.sum()} of {bad.size} out of tolerance; "
+                                 f"worst at {i}: gpu {g[i]:.4e} ref {r[i]:.4e} scale {t[i]:.3e}")
+
+
+def _parity(lens, heads, d, causal, seed=0, scale=None, isolated=False):
+    inp = make_inputs(lens, heads, d, seed=seed)
+    dout = make_dout(inp.q.shape[0], heads, d, seed=seed)
+    scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
+    out = lse = None
+    if isolated:
+        o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
+        out = torch.from_numpy(o_ref).to(torch.bfloat16)
+        lse = torch.from_numpy(l_ref).to(torch.float32).contiguous()
+    got = _gpu_bwd(inp, dout, causal, scale, out, lse)
+    ref, t = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, causal,
+                                       scale, rounding_scale=True)
+    _check(got, ref, t, f"lens={lens} h={heads} d={d} causal={causal} isolated={isolated}")
+    return got
+
+
+RAGGED = [
+    ((1, 1),), ((65, 65),), ((200, 200),), ((129, 129), (1, 1), (64, 64), (300, 300)),
+    ((100, 300),), ((300, 100),), ((70, 0),), ((0, 50), (40, 40)),
+    ((5, 5), (0, 0), (130, 7), (7, 130)),
+]
+
+
+@pytest.mark.parametrize("lens", RAGGED)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_ragged_and_empty(lens, causal, d):
+    _parity(lens, 3, d, causal, seed=len(lens) + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_isolated_from_the_forward(causal):
+    """The backward alone, given the oracle's O and LSE."""
+    _parity(((257, 257), (90, 300), (300, 90)), 2, 128, causal, seed=3, isolated=True)
+
+
+def test_bwd_c1_tiny_dense():
+    w = WORKLOADS["c1_tiny_dense"]
+    inp = workload_inputs(w)
+    dout = make_dout(w.total_q, w.heads, w.head_dim, seed=w.seed)
+    got = _gpu_bwd(inp, dout, w.causal, w.softmax_scale)
+    ref, t = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, w.causal,
+                                       w.softmax_scale, rounding_scale=True)
+    _check(got, ref, t, w.name)
+
+
+def test_bwd_c2_dense_2225_two_heads():
+    """c2's shape (2225 rows, ragged last block) at full length, checked on two of
+    its 16 heads (the oracle's cost); the other heads only for finiteness."""
+    w = WORKLOADS["c2_dense_2225"]
+    inp = workload_inputs(w)
+    dout = make_dout(w.total_q, w.heads, w.head_dim, seed=w.seed)
+    got = _gpu_bwd(inp, dout, w.causal, w.softmax_scale)
+    heads = [0, 11]
+    ref, t = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, w.causal,
+                                       w.softmax_scale, heads=heads, rounding_scale=True)
+    _check([g[:, heads] for g in got], [r[:, heads] for r in ref], [x[:, heads] for x in t],
+           w.name)
+    assert all(np.isfinite(g).all() for g in got)
+
+
+@pytest.mark.parametrize("name", ["c3_varlen_causal_8k", "c4_varlen_causal_32k"])
+def test_bwd_varlen_causal_full_size_sampled(name):
+    """The varlen causal step's shapes at full size, with dO on the scale of the
+    benchmark loss's gradient 2 O / n (n = numel(O)): exactly 2 O / n from the
+    oracle's O on the checked (document, head) pairs, an N(0, 1) draw times
+    2 / n elsewhere. Two documents of one head are checked element by element
+    (the oracle's cost), every gradient for finiteness."""
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    rng = np.random.default_rng(5)
+    docs = sorted({0, int(rng.integers(1, len(w.doc_lens)))})
+    heads = [int(rng.integers(w.heads))]
+    n = w.total_q * w.heads * w.head_dim
+    dout = make_dout(w.total_q, w.heads, w.head_dim, seed=w.seed).float() * (2.0 / n)
+    o_ref, _ = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, w.causal,
+                                w.softmax_scale, heads=heads, docs=docs)
+    for b in docs:
+        q0, q1 = int(inp.cu_q[b]), int(inp.cu_q[b + 1])
+        for h in heads:
+            dout[q0:q1, h] = torch.from_numpy(2.0 * o_ref[q0:q1, h] / n).float()
+    dout = dout.to(torch.bfloat16)
+    got = _gpu_bwd(inp, dout, w.causal, w.softmax_scale)
+    ref, t = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, w.causal,
+                                       w.softmax_scale, heads=heads, docs=docs,
+                                       rounding_scale=True)
+    for b in docs:
+        q0, q1 = int(inp.cu_q[b]), int(inp.cu_q[b + 1])
+        k0, k1 = int(inp.cu_k[b]), int(inp.cu_k[b + 1])
+        sel = [slice(q0, q1), slice(k0, k1), slice(k0, k1)]
+        pick = [lambda x, s=s_: x[s][:, heads] for s_ in sel]
+        _check([f(g) for f, g in zip(pick, got)], [f(r) for f, r in zip(pick, ref)],
+               [f(x) for f, x in zip(pick, t)], f"{name} doc {b} heads {heads}")
+    assert all(np.isfinite(g).all() for g in got)
+
+
+def test_bwd_dense_layout_matches_packed():
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    b, s, h, d = 2, 300, 4, 128
+    inp = make_inputs(((s, s),) * b, h, d, seed=9)
+    dout = make_dout(b * s, h, d, seed=9)
+    packed = _gpu_bwd(inp, dout, True, float(np.float32(1 / np.sqrt(d))))
+    q, k, v = (t.to(dev).reshape(b, s, h, d) for t in (inp.q, inp.k, inp.v))
+    out, lse = fm.fwd(q, k, v, causal=True)
+    dq, dk, dv = fm.bwd(q, k, v, out, dout.to(dev).reshape(b, s, h, d), lse, causal=True)
+    torch.cuda.synchronize()
+    for g, p in zip((dq, dk, dv), packed):
+        assert np.array_equal(g.float().cpu().numpy().reshape(b * s, h, d), p)
+
+
+def test_bwd_deterministic_repeats():
+    inp = make_inputs(((1000, 1000), (777, 777)), 4, 128, seed=21)
+    dout = make_dout(inp.q.shape[0], 4, 128, seed=21)
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    g0 = _gpu_bwd(inp, dout, True, scale)
+    for _ in range(3):
+        g = _gpu_bwd(inp, dout, True, scale)
+        assert all(np.array_equal(a, b) for a, b in zip(g, g0))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_stale_lds_is_never_read(causal):
+    from tests.gpu_support import poison_lds
+    dev = _dev()
+    for lens in (((65, 65),), ((300, 300), (77, 77))):
+        poison_lds(torch.cuda.current_stream(dev).cuda_stream)
+        _parity(lens, 3, 128, causal, seed=41)
