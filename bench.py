@@ -22,6 +22,15 @@ Extra objects on the same line:
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
                 the same workload (whole document x head units), in the same unit.
 
+--step bwd times the backward pass (fmha_bwd, given the forward's O and LSE and
+a fixed upstream gradient dO = 2 O / n, the gradient of the FA4 issue's loss
+mean(O^2)); --step fwd_bwd times the forward followed by the backward, the step
+that issue benchmarks. Backward FLOP are counted as 2.5 times the forward's
+(five products of the forward's size instead of two: S and dP recomputed,
+dV, dK, dQ), the usual convention; the kernels execute seven (dQ recomputes S
+and dP). The roofline object then brackets the whole fmha_bwd call (its three
+launches, on one stream); rocprofv3 summaries give the per-kernel split.
+
 Options: --workload c1|c2|c3|c4|c5 (other workloads, for measurement only:
 x_varlen_noncausal_32k, x_short_q_long_k, x_causal_fp4pv_32k), --splits N|auto
 (the split-KV pass), --trace coarse|detailed (pipeline summary of a traced launch),
@@ -95,6 +104,8 @@ def parse_args():
     ap.add_argument("--trace", choices=["coarse", "detailed"], default=None,
                     help="after the warm-up, one traced launch of the causal ping-pong kernel; "
                          "prints the pipeline summary instead of the throughput line")
+    ap.add_argument("--step", choices=["fwd", "bwd", "fwd_bwd"], default="fwd",
+                    help="what one timed step runs (bf16 workloads for bwd and fwd_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-flop", type=float, default=CPU_SAMPLE_FLOP,
                     help="counted FLOP of the oracle sample (whole document x head units)")
@@ -164,6 +175,37 @@ def make_step(w, d, variant="auto", splits=None):
     return step
 
 
+def make_bwd_step(w, d, with_fwd):
+    """The backward (or forward + backward) step. O and LSE come from one forward
+    pass; dO = 2 O / n (the loss gradient, computed once: it is elementwise work
+    outside the attention) stays fixed, which does not change the work done."""
+    import head_attention_forward_fmha_amd as fm
+    import torch
+    if w.fp8_pv or w.fp4_pv:
+        raise SystemExit("the backward pass is bf16")
+    mq, mk = w.max_seqlen_q, w.max_seqlen_k
+    fwd_args = (d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], mq, mk)
+    fm.fwd(*fwd_args, causal=w.causal, softmax_scale=w.softmax_scale, out=d["out"], lse=d["lse"])
+    n = d["out"].numel()
+    d["dout"] = (d["out"].float() * (2.0 / n)).to(torch.bfloat16)
+    ws = torch.empty(fm.bwd_workspace_size(w.total_q, w.heads), dtype=torch.uint8,
+                     device=d["q"].device)
+    dq, dk, dv = (torch.empty_like(d[x]) for x in ("q", "k", "v"))
+
+    def bwd():
+        fm.bwd(d["q"], d["k"], d["v"], d["out"], d["dout"], d["lse"], d["cu_q"], d["cu_k"], mq,
+               mk, causal=w.causal, softmax_scale=w.softmax_scale, dq=dq, dk=dk, dv=dv,
+               workspace=ws)
+    if not with_fwd:
+        return bwd
+
+    def step():
+        fm.fwd(*fwd_args, causal=w.causal, softmax_scale=w.softmax_scale, out=d["out"],
+               lse=d["lse"])
+        bwd()
+    return step
+
+
 def time_steps(step, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -200,12 +242,13 @@ def load_traffic(w, variant):
     return float(entry["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, inp, sample_flop):
+def cpu_baseline(w, inp, sample_flop, step="fwd"):
     """Time the fp64 oracle on a bounded sample of the workload.
 
     The sample is whole (document, head) units, longest documents first and heads
     in order, until their counted FLOP (the same convention as the GPU figure)
-    reaches sample_flop or the workload is exhausted."""
+    reaches sample_flop or the workload is exhausted. step "bwd" times the
+    backward oracle (with a fixed N(0, 1) dO), "fwd_bwd" both."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
@@ -219,16 +262,25 @@ def cpu_baseline(w, inp, sample_flop):
         v = oracle.mx_dequantize_v(inp.v_e2m1, inp.v_mx_scale, w.head_dim)
     else:
         v = inp.v
+    mult = {"fwd": 1.0, "bwd": 2.5, "fwd_bwd": 3.5}[step]
+    dout = None
+    if step != "fwd":
+        from synthetic import make_dout
+        dout = make_dout(w.total_q, w.heads, w.head_dim, seed=w.seed)
     done, units, parts, dt = 0.0, 0, [], 0.0
     for b in order:
         sq, sk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
-        per_head = 4.0 * sq * sk * w.head_dim / (2.0 if w.causal else 1.0)
+        per_head = mult * 4.0 * sq * sk * w.head_dim / (2.0 if w.causal else 1.0)
         if per_head == 0:
             continue
         n_heads = int(min(w.heads, max(1, np.ceil((sample_flop - done) / per_head))))
         t0 = time.perf_counter()
-        oracle.attention(inp.q, inp.k, v, inp.cu_q, inp.cu_k, w.causal, w.softmax_scale,
-                         heads=list(range(n_heads)), docs=[b])
+        if step != "bwd":
+            oracle.attention(inp.q, inp.k, v, inp.cu_q, inp.cu_k, w.causal, w.softmax_scale,
+                             heads=list(range(n_heads)), docs=[b])
+        if step != "fwd":
+            oracle.attention_backward(inp.q, inp.k, v, dout, inp.cu_q, inp.cu_k, w.causal,
+                                      w.softmax_scale, heads=list(range(n_heads)), docs=[b])
         dt += time.perf_counter() - t0
         done += n_heads * per_head
         units += n_heads
@@ -238,7 +290,7 @@ def cpu_baseline(w, inp, sample_flop):
     return {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{units} (document, head) units: {'; '.join(parts)}; "
-                      f"{done / 1e9:.1f} GFLOP counted, fp64 numpy, {dt:.1f} s wall"}
+                      f"{done / 1e9:.1f} GFLOP counted ({step}), fp64 numpy, {dt:.1f} s wall"}
 
 
 def run_counters(w, d, step):
@@ -332,6 +384,48 @@ def summarize_trace(stats_csv):
     return "\n".join(lines)
 
 
+def bwd_line(w, args, inp, d, step, total_ms, each):
+    """The JSON line of a --step bwd / fwd_bwd run."""
+    import head_attention_forward_fmha_amd as fm
+    mult = 2.5 if args.step == "bwd" else 3.5
+    flops = mult * w.flops()
+    value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    if args.step == "bwd":
+        bwd_ms = sum(each) / len(each)
+    else:
+        # time the backward call alone for the roofline of its kernels
+        bwd = make_bwd_step(w, d, with_fwd=False)
+        _, each_b = time_steps(bwd, max(10, args.steps // 2), 5)
+        bwd_ms = sum(each_b) / len(each_b)
+    achieved = 2.5 * w.flops() / (bwd_ms * 1e-3) / 1e12
+    peak = MI355X_PEAK_TFLOPS["bf16"]
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": f"fmha_bwd call: fmha::fmha_bwd_prep_kernel<{w.head_dim}>, "
+                      f"fmha::fmha_bwd_dkdv_kernel<{w.head_dim}, {str(w.causal).lower()}>, "
+                      f"fmha::fmha_bwd_dq_kernel<{w.head_dim}, {str(w.causal).lower()}>",
+            "launch_avg_us": round(bwd_ms * 1e3, 2),
+            "algorithmic_flop_per_launch": 2.5 * w.flops()}
+    line = {
+        "metric": ("FMHA bwd" if args.step == "bwd" else "FMHA fwd+bwd") +
+                  " TFLOP/s (bwd counted as 2.5x the fwd FLOP), d=%d, 1 GPU" % w.head_dim,
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
+        "median_ms": round(each[len(each) // 2], 4), "min_ms": round(each[0], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.description, "name": w.name, "total_tokens": w.total_q,
+                   "docs": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "causal": w.causal, "seed": w.seed, "step": args.step,
+                   "kernel_variant": fm.auto_variant(w.batch, w.max_seqlen_q, w.heads)},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_flop, args.step)
+    return line
+
+
 def main():
     args = parse_args()
     if args.summarize_trace:
@@ -380,7 +474,12 @@ def main():
     w = {**WORKLOADS, **EXTRA_WORKLOADS}[name]
     dev = torch.device("cuda:0")
     inp, d = device_inputs(w, dev)
-    step = make_step(w, d, args.variant, args.splits)
+    if args.step == "fwd":
+        step = make_step(w, d, args.variant, args.splits)
+    else:
+        if args.splits is not None or args.trace or args.variant != "auto":
+            raise SystemExit("--step bwd/fwd_bwd runs the default forward variant, unsplit")
+        step = make_bwd_step(w, d, with_fwd=args.step == "fwd_bwd")
     if args.counters:
         run_counters(w, d, step)
         return
@@ -388,6 +487,9 @@ def main():
         run_trace(w, d, step, args)
         return
     total_ms, each = time_steps(step, args.steps, args.warmup)
+    if args.step != "fwd":
+        print(json.dumps(bwd_line(w, args, inp, d, step, total_ms, each)), flush=True)
+        return
     flops = w.flops()
     ms_per_step = total_ms / args.steps
     value = flops * args.steps / (total_ms * 1e-3) / 1e12

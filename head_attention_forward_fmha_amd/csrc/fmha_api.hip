@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include "fmha.h"
+#include "fmha_bwd_params.h"
 #include "fmha_kernel_params.h"
 
 static_assert(FMHA_TRACE_EVENTS_PER_WAVE == fmha::kTraceEvents, "trace record count");

@@ -31,6 +31,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "fmha_bwd_params.h"
 #include "fmha_device.h"
 
 namespace fmha {
