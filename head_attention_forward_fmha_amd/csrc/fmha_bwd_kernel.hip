@@ -359,7 +359,7 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
 
 template <int kD, bool kCausal>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdWaves * 64, kBwdWaves * 64),
-                          amdgpu_waves_per_eu(1, 1)))
+                          amdgpu_waves_per_eu(2, 2)))
 void fmha_bwd_dq_kernel(BwdParams p) {
   using G = TileGeom<kD>;
   __shared__ __attribute__((aligned(1024))) char smem_k[2][G::kTileBytes];
@@ -415,49 +415,77 @@ void fmha_bwd_dq_kernel(BwdParams p) {
     constexpr int st = decltype(stage_tag)::value;
     const char* ks = smem_k[st];
     const char* vs = smem_v[st];
-    // S^T = K Q^T, dP^T = V dO^T: keys 32*kb + 8(r/4) + 4*half + r%4 of the
-    // tile by this lane's query
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
-#pragma unroll
-    for (int t = 0; t < G::kKSteps; ++t)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int off = tl.row_off[t] + kb * 32 * G::kRowBytes;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ks + off), qreg[t],
-                                                        s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vs + off), doreg[t],
-                                                         dp[kb], 0, 0, 0);
-      }
     const int k0 = j * kTileRows;
     const bool need_mask = (k0 + kTileRows > w.sk) || (kCausal && k0 + kTileRows - 1 > wave_q0 + causal_off);
+    // One 32-key block at a time (which keeps two waves per SIMD within their
+    // registers): S^T = K Q^T and dP^T = V dO^T for keys 32*kb + 8(r/4) +
+    // 4*half + r%4 of the tile by this lane's query, then dS^T in bf16.
     bf16x8 dsb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      // operands read two steps ahead of their MFMAs (a ring of three), and the
+      // scheduling-group barriers keep the reads from being hoisted further
+      constexpr int kAhead = 2;
+      bf16x8 ka[kAhead + 1], va[kAhead + 1];
+      auto read = [&](int t) {
+        const int off = tl.row_off[t] + kb * 32 * G::kRowBytes;
+        ka[t % (kAhead + 1)] = *(const bf16x8*)(ks + off);
+        va[t % (kAhead + 1)] = *(const bf16x8*)(vs + off);
+      };
+#pragma unroll
+      for (int t = 0; t < kAhead; ++t) read(t);
+#pragma unroll
+      for (int t = 0; t < G::kKSteps; ++t) {
+        if (t + kAhead < G::kKSteps) read(t + kAhead);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kAhead + 1)], qreg[t], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % (kAhead + 1)], doreg[t], dp, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+      for (int t = 0; t < G::kKSteps; ++t) {
+        if (t + kAhead < G::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2));
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
         if (need_mask) {
           const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
           if (key >= w.sk || (kCausal && key > qi + causal_off)) pv = 0.f;
         }
-        dsb[2 * kb + r / 8][r % 8] = (bf16_t)(pv * (dp[kb][r] - delta));
+        dsb[2 * kb + r / 8][r % 8] = (bf16_t)(pv * (dp[r] - delta));
       }
-    // dQ^T += K^T dS^T (transposed K tile reads)
+    }
+    // dQ^T += K^T dS^T (transposed K tile reads, three MFMAs ahead)
+    constexpr int kN = 4 * G::kDBlocks;
+    constexpr int kAhead = 3;
+    bf16x8 ta[kAhead + 1];
+    auto read_t = [&](int i) {
+      const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (LDS_AS bf16x4*)(ks + tl.tr_off[0][db] + 16 * ks16 * G::kRowBytes));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (LDS_AS bf16x4*)(ks + tl.tr_off[1][db] + 16 * ks16 * G::kRowBytes));
+      ta[i % (kAhead + 1)] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
 #pragma unroll
-    for (int ks16 = 0; ks16 < 4; ++ks16)
+    for (int i = 0; i < kAhead; ++i) read_t(i);
 #pragma unroll
-      for (int db = 0; db < G::kDBlocks; ++db) {
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(ks + tl.tr_off[0][db] + 16 * ks16 * G::kRowBytes));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(ks + tl.tr_off[1][db] + 16 * ks16 * G::kRowBytes));
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[ks16], dqacc[db], 0, 0, 0);
-      }
+    for (int i = 0; i < kN; ++i) {
+      if (i + kAhead < kN) read_t(i + kAhead);
+      const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
+      dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i % (kAhead + 1)], dsb[ks16],
+                                                          dqacc[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
   };
 
   auto step = [&](int j, auto stage_tag) {
