@@ -116,6 +116,9 @@ def parse_args():
                          "WRITE_SIZE) of a --counters run into an entry of the traffic file")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="print a rocprofv3 --stats kernel_stats.csv as a text table")
+    ap.add_argument("--microbench", action="store_true",
+                    help="instead of a step: instruction-throughput microbenchmarks (exp2, FMA, "
+                         "P conversions, MFMA, LDS reads and their overlap), one JSON line")
     return ap.parse_args()
 
 
@@ -465,6 +468,18 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.microbench:
+        if not torch.cuda.is_available():
+            raise SystemExit("bench.py --microbench needs a GPU")
+        from head_attention_forward_fmha_amd import microbench
+        props = torch.cuda.get_device_properties(0)
+        cus = props.multi_processor_count
+        rows = microbench.run_all(cus)
+        print(json.dumps({"microbench": "instruction throughput in isolation", "device": props.name,
+                          "gcn_arch": getattr(props, "gcnArchName", ""), "cus": cus,
+                          "cycles": "shader clock (s_memtime), per wave, median over the device",
+                          "rows": rows}))
+        return
     from synthetic import EXTRA_WORKLOADS, WORKLOADS
     import head_attention_forward_fmha_amd as fm
     if not torch.cuda.is_available():

@@ -1,4 +1,5 @@
-"""Builds libfmha.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Builds libfmha.so (HIP kernels + C ABI) and libfmha_microbench.so (the
+instruction-throughput microbenchmarks) for gfx950 with hipcc, in-tree.
 
 Usage: python -m head_attention_forward_fmha_amd.build [--verbose]
 
@@ -26,6 +27,9 @@ LIB_NAME = "libfmha.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 RESOURCE_REPORT = os.path.join(PKG_DIR, "libfmha.resource-usage.txt")
 SOURCES = ["fmha_fwd_kernel.hip", "fmha_merge.hip", "fmha_bwd_kernel.hip", "fmha_api.hip"]
+# instruction-throughput microbenchmarks (measurement support, include/fmha_microbench.h)
+MICROBENCH_SOURCE = "microbench.hip"
+MICROBENCH_LIB_PATH = os.path.join(PKG_DIR, "libfmha_microbench.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -105,6 +109,18 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}")
         reports.append(r.stderr)
         objs.append(obj)
+    # the microbenchmark library: one source, its own shared object
+    obj = os.path.join(build_dir, MICROBENCH_SOURCE + ".o")
+    cmd = [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, MICROBENCH_SOURCE), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {MICROBENCH_SOURCE}")
+    reports.append(r.stderr)
+    mb_obj = obj
     rpaths = [d for d in (_torch_lib_dir(), "/opt/rocm/lib") if d]
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
@@ -116,6 +132,14 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link of libfmha.so failed")
     os.replace(tmp, LIB_PATH)
+    tmp = MICROBENCH_LIB_PATH + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, mb_obj,
+           *[f"-Wl,-rpath,{d}" for d in rpaths]]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of libfmha_microbench.so failed")
+    os.replace(tmp, MICROBENCH_LIB_PATH)
     text = "\n".join(reports)
     with open(RESOURCE_REPORT, "w") as f:
         f.write(text)
