@@ -98,14 +98,15 @@ struct TileLane {
 
   // copy of the 64 rows from row0 on (relative to the descriptor's base) into
   // the tile at LDS address lds_wave0 + kLdsOffset (lds_wave0: this wave's first
-  // 1 KB block of stage 0)
+  // 1 KB block of stage 0). The rows' offset goes into the per-lane offset,
+  // which the raw-buffer range check covers, so rows past the end read zeros.
   template <int kLdsOffset>
   __device__ __forceinline__ void copy(uint32_t lds_wave0, i32x4 rsrc, int row0,
                                        uint32_t stride) const {
-    const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)row0 * stride));
+    const int off = __builtin_amdgcn_readfirstlane((int)((uint32_t)row0 * stride));
     static_for<G::kLoads>([&](auto r_tag) {
       constexpr int r = decltype(r_tag)::value;
-      lds_dma_16<kLdsOffset + 1024 * kBwdWaves * r>(lds_wave0, copy_off[r], rsrc, soff);
+      lds_dma_16<kLdsOffset + 1024 * kBwdWaves * r>(lds_wave0, copy_off[r] + off, rsrc, 0);
     });
   }
 };

@@ -116,8 +116,10 @@ constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 
 constexpr int waitcnt_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
 // Buffer resource (V#) for raw byte-addressed loads: base, size in bytes, and
-// the gfx9 raw-buffer format word. Loads at offsets >= num_bytes return zero,
-// which is how rows past the end of a document are filled.
+// the gfx9 raw-buffer format word. Loads whose per-lane offset (plus the
+// instruction's immediate offset) is >= num_bytes return zero, which is how
+// rows past the end of a document are filled; the copies keep the scalar
+// offset at zero, so every byte address is covered by that check.
 __device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base, uint32_t num_bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
@@ -513,17 +515,19 @@ struct WaveTile {
   // This wave's share of the copy of K tile j into K stage kStage (lds_k0 is
   // the LDS address of this wave's first 1 KB block in stage 0): instruction r
   // of kLoadsPerWave, or all of them. V likewise.
+  // The tile's byte offset goes into the per-lane offset, not the scalar one:
+  // the raw-buffer range check that turns rows past the document end into
+  // zeros is made on the per-lane offset, so every byte of the copy is checked
+  // against the buffer's size.
   template <int kStage, int kR>
   __device__ __forceinline__ void copy_k_one(int j, uint32_t lds_k0) {
     lds_dma_16<kStage * kTileBytes + 1024 * kWaves * kR>(
-        lds_k0, k_voff[kR], k_rsrc,
-        scalar_offset((int)((uint32_t)(j * kBN) * k_stride)));
+        lds_k0, k_voff[kR] + scalar_offset((int)((uint32_t)(j * kBN) * k_stride)), k_rsrc, 0);
   }
   template <int kStage, int kR>
   __device__ __forceinline__ void copy_v_one(int j, uint32_t lds_v0) {
     lds_dma_16<kStage * kVStageBytes + 1024 * kWaves * kR>(
-        lds_v0, v_voff[kR], v_rsrc,
-        scalar_offset((int)((uint32_t)(j * kBN) * v_stride)));
+        lds_v0, v_voff[kR] + scalar_offset((int)((uint32_t)(j * kBN) * v_stride)), v_rsrc, 0);
   }
   // e2m1 V: tile j's exponent image (the same 256 bytes from every wave)
   template <int kStage>

@@ -124,6 +124,7 @@ def summarize(trace, clock_ghz: float | None = None) -> dict:
     counts = {k: len(v) for k, v in acc.items()}
     out = {"waves": waves, "cycles_per_wave": total / waves if waves else None,
            "mean_cycles": mean, "count": counts}
+    out["critical"] = critical_path(trace)
     if mean["mfma_busy"] is not None and mean["valu_busy"] is not None:
         mslot = mean["mfma_busy"] + mean["mfma_wait"]
         vslot = mean["valu_busy"] + mean["valu_wait"]
@@ -136,3 +137,48 @@ def summarize(trace, clock_ghz: float | None = None) -> dict:
         if clock_ghz:
             out["period_ns"] = out["period"] / clock_ghz
     return out
+
+
+def critical_path(trace) -> dict:
+    """Which phase ends each slot, from the stamps of all eight waves of a workgroup.
+
+    Every wave of a workgroup passes the same barriers, so slot k of each wave
+    is the same interval (coarse and detailed records both stamp every slot of
+    every wave alike). Per steady slot with four MFMA-role and four VALU-role
+    waves: t0 = the earliest slot start; mfma_last and valu_last = the latest
+    phase-done stamp of each role, relative to t0; release = the latest slot end
+    (the next barrier's release), relative to t0. The VALU role's done stamp is
+    taken after its softmax and before it waits for its copies, so release -
+    max(mfma_last, valu_last) holds that copy wait and the barrier itself.
+    Returns the means and valu_share, the fraction of slots whose last phase
+    to finish was a VALU phase.
+    """
+    trace = np.asarray(trace, dtype=np.uint64)
+    m_last, v_last, rel, gap, v_crit = [], [], [], [], []
+    for wg in range(trace.shape[0]):
+        per_wave = [_slots(decode_wave(trace[wg, w])) for w in range(trace.shape[1])]
+        if any(len(sl) == 0 for sl in per_wave):
+            continue
+        n = min(len(sl) for sl in per_wave)
+        for k in range(n):
+            slot = [sl[k] for sl in per_wave]
+            if any(x[0] not in ("mfma", "valu") for x in slot):
+                continue
+            mf = [x for x in slot if x[0] == "mfma"]
+            va = [x for x in slot if x[0] == "valu"]
+            if len(mf) != 4 or len(va) != 4:
+                continue
+            t0 = min(x[1] for x in slot)
+            ml = max(x[3][EV_MFMA_DONE] for x in mf) - t0
+            vl = max(x[3][EV_VALU_DONE] for x in va) - t0
+            r = max(x[2] for x in slot) - t0
+            m_last.append(ml)
+            v_last.append(vl)
+            rel.append(r)
+            gap.append(r - max(ml, vl))
+            v_crit.append(1.0 if vl > ml else 0.0)
+    if not rel:
+        return {"slots": 0}
+    return {"slots": len(rel), "mfma_last": float(np.mean(m_last)),
+            "valu_last": float(np.mean(v_last)), "release": float(np.mean(rel)),
+            "after_last_done": float(np.mean(gap)), "valu_share": float(np.mean(v_crit))}

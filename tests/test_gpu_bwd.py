@@ -208,3 +208,40 @@ def test_bwd_stale_lds_is_never_read(causal):
     for lens in (((65, 65),), ((300, 300), (77, 77))):
         poison_lds(torch.cuda.current_stream(dev).cuda_stream)
         _parity(lens, 3, 128, causal, seed=41)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_rows_after_the_last_document_are_never_read(causal):
+    """Q, K, V, O and dO are views of the first rows of buffers whose next 128
+    rows hold NaN. Both documents end inside a 64-row tile, so the backward's
+    tile copies reach past the last row; they must read zeros (the buffer range
+    check), never the NaN rows, which would spread NaN into dQ, dK and dV."""
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    heads, d, pad = 2, 128, 128
+    lens = ((50, 70), (90, 77))               # total_q = 140, total_k = 147
+    inp = make_inputs(lens, heads, d, seed=37)
+    dout = make_dout(inp.q.shape[0], heads, d, seed=37)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    cq, ck = _cu(inp.cu_q, dev), _cu(inp.cu_k, dev)
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
+
+    def padded(x):
+        buf = torch.full((x.shape[0] + pad,) + tuple(x.shape[1:]), float("nan"),
+                         dtype=torch.bfloat16, device=dev)
+        buf[:x.shape[0]] = x.to(dev)
+        return buf[:x.shape[0]]
+
+    q, k, v = padded(inp.q), padded(inp.k), padded(inp.v)
+    out = padded(torch.from_numpy(o_ref).to(torch.bfloat16))
+    lse = torch.from_numpy(l_ref).to(torch.float32).contiguous().to(dev)
+    do = padded(dout)
+    nan = float("nan")
+    dq, dk, dv = torch.full_like(q, nan), torch.full_like(k, nan), torch.full_like(v, nan)
+    fm.bwd(q, k, v, out, do, lse, cq, ck, 90, 77, causal=causal, softmax_scale=scale,
+           dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    ref, t = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, causal,
+                                       scale, rounding_scale=True)
+    _check(got, ref, t, f"NaN-padded inputs, causal={causal}")

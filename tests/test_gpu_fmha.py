@@ -328,3 +328,44 @@ def test_stale_lds_is_never_read(variant, causal, d):
     for lens in (((65, 65),), ((130, 130),), ((300, 300), (77, 77))):
         poison_lds(torch.cuda.current_stream(dev).cuda_stream)
         _full_parity(lens, 3, d, causal, seed=41, variant=variant)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("variant", VARIANTS_FP8)
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_after_the_last_document_are_never_read(fp8, variant, causal):
+    """K and V are views of the first total_k rows of buffers whose next 128
+    rows hold NaN (e4m3 NaN codes for fp8 V). The last document ends inside a
+    64-key tile, so its last tile's copies reach past total_k; they must read
+    zeros (the buffer range check), never the NaN rows, which would turn O into
+    NaN through P = 0 times NaN."""
+    import head_attention_forward_fmha_amd as fm
+    dev = _dev()
+    heads, d = 2, 128
+    lens = ((50, 70), (90, 77))               # total_k = 147: 19 keys into its third tile
+    inp = make_inputs(lens, heads, d, seed=31, fp8_pv=fp8)
+    total_q, total_k = inp.q.shape[0], inp.k.shape[0]
+    pad = 128
+    k_buf = torch.full((total_k + pad, heads, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    k_buf[:total_k] = inp.k.to(dev)
+    k = k_buf[:total_k]
+    cq = torch.from_numpy(np.asarray(inp.cu_q, np.int32)).to(dev)
+    ck = torch.from_numpy(np.asarray(inp.cu_k, np.int32)).to(dev)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    if fp8:
+        v_buf = torch.full((total_k + pad, heads, d), 0x7F, dtype=torch.uint8, device=dev)
+        v_buf[:total_k] = inp.v_e4m3.to(dev)
+        o, lse = fm.fwd_fp8pv(inp.q.to(dev), k, v_buf[:total_k], inp.v_scale.to(dev), cq, ck, 90,
+                              77, causal=causal, softmax_scale=scale, variant=variant)
+        o_ref, l_ref = oracle.attention_fp8pv(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                              inp.cu_k, causal, scale)
+    else:
+        v_buf = torch.full((total_k + pad, heads, d), float("nan"), dtype=torch.bfloat16,
+                           device=dev)
+        v_buf[:total_k] = inp.v.to(dev)
+        o, lse = fm.fwd(inp.q.to(dev), k, v_buf[:total_k], cq, ck, 90, 77, causal=causal,
+                        softmax_scale=scale, variant=variant)
+        o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
+    torch.cuda.synchronize()
+    _check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+           o_ref, l_ref, fp8=fp8, what=f"NaN-padded K/V, fp8={fp8}, {variant}")

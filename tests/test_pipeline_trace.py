@@ -81,3 +81,29 @@ def test_detailed_summary_splits_the_phases():
     assert m["qk"] == 250 and m["pv"] == 250
     assert m["copy"] == 40 and m["softmax"] == 480
     assert m["copy_wait"] == 30 and m["barrier"] == 70
+
+
+def _trace_with(mb, mw, vb, vw):
+    tr = np.zeros((2, 8, 512), dtype=np.uint64)
+    for wg in range(2):
+        for wave in range(8):
+            recs = _wave(5, wave < 4, False, mb=mb, mw=mw, vb=vb, vw=vw)
+            tr[wg, wave, :len(recs)] = recs
+    return tr
+
+
+def test_critical_path_names_the_later_phase():
+    # every slot lasts 620 cycles; the VALU phase is done at 520, the MFMA phase at 500
+    c = pt.critical_path(_trace_with(500, 120, 520, 100))
+    assert c["slots"] == 2 * 2 * 2 * 6        # workgroups x items x slot pairs x 2
+    assert c["mfma_last"] == 500 and c["valu_last"] == 520 and c["release"] == 620
+    assert c["after_last_done"] == 100 and c["valu_share"] == 1.0
+    # the MFMA phase is done later
+    c = pt.critical_path(_trace_with(560, 60, 520, 100))
+    assert c["mfma_last"] == 560 and c["after_last_done"] == 60 and c["valu_share"] == 0.0
+    # the summary carries it
+    assert pt.summarize(_trace_with(500, 120, 520, 100))["critical"]["valu_share"] == 1.0
+
+
+def test_critical_path_of_an_empty_trace():
+    assert pt.critical_path(np.zeros((1, 8, 16), dtype=np.uint64)) == {"slots": 0}
