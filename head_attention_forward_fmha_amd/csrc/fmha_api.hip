@@ -43,9 +43,11 @@ fmha_status_t check_common(const void* q, const void* k, const void* v,
     // dense [batch, seqlen, heads, d]
     if ((int64_t)batch * max_q != total_q || (int64_t)batch * max_k != total_k) return FMHA_ERR_INVALID_ARG;
   }
-  // element offsets are computed in 32-bit inside the kernels' inner loops
+  // element offsets are computed in 32-bit inside the kernels' inner loops, and
+  // a tile copy's per-lane byte offset reaches up to 63 rows past a document's
+  // end (those rows read as zeros only while that offset does not wrap)
   const int64_t row = (int64_t)heads * head_dim;
-  if (row * (int64_t)total_q > INT32_MAX || row * (int64_t)total_k > INT32_MAX ||
+  if (row * ((int64_t)total_q + 64) > INT32_MAX || row * ((int64_t)total_k + 64) > INT32_MAX ||
       (int64_t)heads * total_q > INT32_MAX || batch > 65535 || heads > 65535 ||
       ((int64_t)max_q + 127) / 128 * heads * batch > INT32_MAX)
     return FMHA_ERR_UNSUPPORTED;

@@ -37,7 +37,10 @@
  * Errors. Argument checks run on the host before any HIP call and return
  * FMHA_ERR_INVALID_ARG (null or misaligned pointers, negative sizes,
  * inconsistent dense sizes, non-finite scale) or FMHA_ERR_UNSUPPORTED (a
- * head_dim other than 64 or 128). A failed launch returns FMHA_ERR_LAUNCH. The
+ * head_dim other than 64 or 128, or a problem beyond the kernels' 32-bit
+ * offsets: heads * head_dim * (total_q + 64) or heads * head_dim * (total_k +
+ * 64) above 2^31 - 1, heads * total_q above 2^31 - 1, batch or heads above
+ * 65535). A failed launch returns FMHA_ERR_LAUNCH. The
  * contents of cu_seqlens are a precondition (non-decreasing, starting at 0,
  * ending at total, every length <= max_seqlen); they are not read on the host,
  * and fmha_validate_cu_seqlens checks a host copy. Behaviour on violated

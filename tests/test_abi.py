@@ -79,6 +79,10 @@ def _call_fwd(**kw):
     (dict(total_q=100), 1),        # dense: total != batch * max_seqlen
     (dict(cu_q=0x60000), 1),       # only one cu_seqlens pointer
     (dict(heads=70000), 2),
+    # 32-bit offsets: heads * d * (total + 64) must stay below 2^31 (here 2 * 64: 16777152
+    # is the first total past it; the limit without the 64-row headroom took it)
+    (dict(total_k=16777152, max_k=16777152), 2),
+    (dict(total_q=16777152, max_q=16777152), 2),
 ])
 def test_fwd_rejects_bad_arguments(kw, status):
     assert _call_fwd(**kw) == status
