@@ -267,16 +267,40 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
+    {
+      // operands read two steps ahead of their MFMAs (a ring of three), the
+      // scheduling-group barriers keeping the reads from being pulled back next
+      // to their uses: with one wave per SIMD nothing else hides an LDS round trip
+      constexpr int kAhead = 2;
+      bf16x8 qa[kAhead + 1][2], da[kAhead + 1][2];
+      auto read_rows = [&](int t) {
 #pragma unroll
-    for (int t = 0; t < G::kKSteps; ++t)
+        for (int kb = 0; kb < 2; ++kb) {
+          const int off = tl.row_off[t] + kb * 32 * G::kRowBytes;
+          qa[t % (kAhead + 1)][kb] = *(const bf16x8*)(qs + off);
+          da[t % (kAhead + 1)][kb] = *(const bf16x8*)(dos + off);
+        }
+      };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int off = tl.row_off[t] + kb * 32 * G::kRowBytes;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + off), kreg[t],
-                                                        s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(dos + off), vreg[t],
-                                                         dp[kb], 0, 0, 0);
+      for (int t = 0; t < kAhead; ++t) read_rows(t);
+#pragma unroll
+      for (int t = 0; t < G::kKSteps; ++t) {
+        if (t + kAhead < G::kKSteps) read_rows(t + kAhead);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t % (kAhead + 1)][kb], kreg[t],
+                                                          s[kb], 0, 0, 0);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t % (kAhead + 1)][kb], vreg[t],
+                                                           dp[kb], 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * kAhead, 0);
+#pragma unroll
+      for (int t = 0; t < G::kKSteps; ++t) {
+        if (t + kAhead < G::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+    }
     // P = exp2(S*c - LSE*log2e), dS = P (dP - D); masked keys get P = 0.
     // Register r of block kb is query 32*kb + 8*(r/4) + 4*half + r%4; P and dS
     // are rounded to bf16 as the B operands of the transposed products, 16
@@ -306,22 +330,41 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
           dsb[2 * kb + r / 8][r % 8] = (bf16_t)ds;
         }
       }
-    // dV^T += dO^T P and dK^T += Q^T dS (transposed tile reads)
-#pragma unroll
-    for (int ks16 = 0; ks16 < 4; ++ks16)
-#pragma unroll
-      for (int db = 0; db < G::kDBlocks; ++db) {
+    // dV^T += dO^T P and dK^T += Q^T dS (transposed tile reads, three MFMA
+    // pairs ahead of their use)
+    {
+      constexpr int kN = 4 * G::kDBlocks;   // (16-query step, d block) pairs
+      constexpr int kAhead = 3;
+      bf16x8 ad[kAhead + 1], aq[kAhead + 1];
+      auto read_t = [&](int i) {
+        const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
         const int o0 = tl.tr_off[0][db] + 16 * ks16 * G::kRowBytes;
         const int o1 = tl.tr_off[1][db] + 16 * ks16 * G::kRowBytes;
         const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o0));
         const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o1));
         const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o0));
         const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o1));
-        const bf16x8 ad = {dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
-        const bf16x8 aq = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pb[ks16], dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[ks16], dkacc[db], 0, 0, 0);
+        ad[i % (kAhead + 1)] = bf16x8{dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
+        aq[i % (kAhead + 1)] = bf16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+      };
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) read_t(i);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        if (i + kAhead < kN) read_t(i + kAhead);
+        const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[i % (kAhead + 1)], pb[ks16],
+                                                            dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i % (kAhead + 1)], dsb[ks16],
+                                                            dkacc[db], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * kAhead, 1);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      }
+    }
   };
 
   // double-buffered tile loop: tile jt lives in stage (jt - t0) & 1
