@@ -254,115 +254,149 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
     lds_dma_global_4(rl + kTileRows * 4, p.delta + r);
   };
 
-  auto compute = [&](int jt, auto stage_tag) {
+  // One query tile (64 rows) against this wave's 32 keys, software-pipelined
+  // within the wave, since no other wave on the SIMD hides its vector work: S
+  // and dP of query block 0; then S and dP of block 1 interleaved with block 0's
+  // P and dS; then block 1's P and dS interleaved with the dV/dK products that
+  // need only block 0 (16-query steps 0 and 1); then the other products. kMask:
+  // the tile needs the causal mask or the query tail; it is chosen outside, so
+  // that no branch splits the interleaved stream.
+  auto compute = [&](int jt, auto stage_tag, auto mask_tag) {
     constexpr int st = decltype(stage_tag)::value;
+    constexpr bool kMask = decltype(mask_tag)::value;
     const char* qs = smem_q[st];
     const char* dos = smem_do[st];
     const float* rows = smem_rows[st];
     const int q0 = jt * kTileRows;
-    // S = Q K^T and dP = dO V^T: rows 32*kb + 8(r/4) + 4*half + r%4 of the tile
-    // (queries) by this lane's key
+    const int key = kw0 + col;
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
-    {
-      // operands read two steps ahead of their MFMAs (a ring of three), the
-      // scheduling-group barriers keeping the reads from being pulled back next
-      // to their uses: with one wave per SIMD nothing else hides an LDS round trip
+    bf16x8 pb[4], dsb[4];
+
+    // S = Q K^T and dP = dO V^T of query block kb: rows 32*kb + 8(r/4) +
+    // 4*half + r%4 of the tile by this lane's key, operands two steps ahead of
+    // their MFMAs (a ring of three)
+    auto sdp = [&](auto kb_tag) {
+      constexpr int kb = decltype(kb_tag)::value;
       constexpr int kAhead = 2;
-      bf16x8 qa[kAhead + 1][2], da[kAhead + 1][2];
+      bf16x8 qa[kAhead + 1], da[kAhead + 1];
       auto read_rows = [&](int t) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = tl.row_off[t] + kb * 32 * G::kRowBytes;
-          qa[t % (kAhead + 1)][kb] = *(const bf16x8*)(qs + off);
-          da[t % (kAhead + 1)][kb] = *(const bf16x8*)(dos + off);
-        }
+        const int off = tl.row_off[t] + kb * 32 * G::kRowBytes;
+        qa[t % (kAhead + 1)] = *(const bf16x8*)(qs + off);
+        da[t % (kAhead + 1)] = *(const bf16x8*)(dos + off);
       };
 #pragma unroll
       for (int t = 0; t < kAhead; ++t) read_rows(t);
 #pragma unroll
       for (int t = 0; t < G::kKSteps; ++t) {
         if (t + kAhead < G::kKSteps) read_rows(t + kAhead);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t % (kAhead + 1)][kb], kreg[t],
-                                                          s[kb], 0, 0, 0);
-          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t % (kAhead + 1)][kb], vreg[t],
-                                                           dp[kb], 0, 0, 0);
-        }
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t % (kAhead + 1)], kreg[t], s[kb], 0,
+                                                        0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t % (kAhead + 1)], vreg[t], dp[kb], 0,
+                                                         0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * kAhead, 0);
-#pragma unroll
-      for (int t = 0; t < G::kKSteps; ++t) {
-        if (t + kAhead < G::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
-    }
-    // P = exp2(S*c - LSE*log2e), dS = P (dP - D); masked keys get P = 0.
-    // Register r of block kb is query 32*kb + 8*(r/4) + 4*half + r%4; P and dS
-    // are rounded to bf16 as the B operands of the transposed products, 16
-    // queries per MFMA, in the order the forward uses for its P.
-    const bool need_mask = (q0 + kTileRows > w.sq) || (kCausal && kw0 + 31 > q0 + causal_off);
-    const int key = kw0 + col;
-    bf16x8 pb[4], dsb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    };
+    // LSE*log2e and D of the 16 queries of block kb this lane's registers hold
+    auto read_rowvals = [&](int kb, float (&lv)[16], float (&dl)[16]) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qr = 32 * kb + 8 * g4 + 4 * half;
         const float4 l4 = *(const float4*)(rows + qr);
         const float4 d4 = *(const float4*)(rows + kTileRows + qr);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+        lv[4 * g4 + 0] = l4.x; lv[4 * g4 + 1] = l4.y; lv[4 * g4 + 2] = l4.z; lv[4 * g4 + 3] = l4.w;
+        dl[4 * g4 + 0] = d4.x; dl[4 * g4 + 1] = d4.y; dl[4 * g4 + 2] = d4.z; dl[4 * g4 + 3] = d4.w;
+      }
+    };
+    // P = exp2(S*c - LSE*log2e), dS = P (dP - D) of block kb; masked keys get
+    // P = 0. Both are rounded to bf16 as the B operands of the transposed
+    // products, 16 queries per MFMA, in the order the forward uses for its P.
+    auto pds = [&](auto kb_tag, const float (&lv)[16], const float (&dl)[16]) {
+      constexpr int kb = decltype(kb_tag)::value;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lv[e]));
-          if (need_mask) {
-            const int i = q0 + qr + e;
-            if (i >= w.sq || (kCausal && key > i + causal_off)) pv = 0.f;
-          }
-          const float ds = pv * (dp[kb][r] - dl[e]);
-          pb[2 * kb + r / 8][r % 8] = (bf16_t)pv;
-          dsb[2 * kb + r / 8][r % 8] = (bf16_t)ds;
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lv[r]));
+        if constexpr (kMask) {
+          const int i = q0 + 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
+          if (i >= w.sq || (kCausal && key > i + causal_off)) pv = 0.f;
         }
+        const float ds = pv * (dp[kb][r] - dl[r]);
+        pb[2 * kb + r / 8][r % 8] = (bf16_t)pv;
+        dsb[2 * kb + r / 8][r % 8] = (bf16_t)ds;
       }
-    // dV^T += dO^T P and dK^T += Q^T dS (transposed tile reads, three MFMA
-    // pairs ahead of their use)
-    {
-      constexpr int kN = 4 * G::kDBlocks;   // (16-query step, d block) pairs
-      constexpr int kAhead = 3;
-      bf16x8 ad[kAhead + 1], aq[kAhead + 1];
-      auto read_t = [&](int i) {
-        const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
-        const int o0 = tl.tr_off[0][db] + 16 * ks16 * G::kRowBytes;
-        const int o1 = tl.tr_off[1][db] + 16 * ks16 * G::kRowBytes;
-        const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o0));
-        const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o1));
-        const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o0));
-        const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o1));
-        ad[i % (kAhead + 1)] = bf16x8{dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
-        aq[i % (kAhead + 1)] = bf16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-      };
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS: pair i (16-query step i / kDBlocks,
+    // d block i % kDBlocks) reads the tiles transposed, three pairs ahead
+    constexpr int kN = 4 * G::kDBlocks;
+    constexpr int kAheadT = 3;
+    bf16x8 ad[kAheadT + 1], aq[kAheadT + 1];
+    auto read_t = [&](int i) {
+      const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
+      const int o0 = tl.tr_off[0][db] + 16 * ks16 * G::kRowBytes;
+      const int o1 = tl.tr_off[1][db] + 16 * ks16 * G::kRowBytes;
+      const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o0));
+      const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o1));
+      const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o0));
+      const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o1));
+      ad[i % (kAheadT + 1)] = bf16x8{dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
+      aq[i % (kAheadT + 1)] = bf16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+    };
+    auto dvdk = [&](int i) {
+      if (i + kAheadT < kN) read_t(i + kAheadT);
+      const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
+      dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[i % (kAheadT + 1)], pb[ks16],
+                                                          dvacc[db], 0, 0, 0);
+      dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i % (kAheadT + 1)], dsb[ks16],
+                                                          dkacc[db], 0, 0, 0);
+    };
+
+    float lv[16], dl[16];
+    sdp(std::integral_constant<int, 0>());
+    read_rowvals(0, lv, dl);
+    sdp(std::integral_constant<int, 1>());
+    pds(std::integral_constant<int, 0>(), lv, dl);
+    read_rowvals(1, lv, dl);
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) read_t(i);
+    for (int i = 0; i < kAheadT; ++i) read_t(i);
 #pragma unroll
-      for (int i = 0; i < kN; ++i) {
-        if (i + kAhead < kN) read_t(i + kAhead);
-        const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[i % (kAhead + 1)], pb[ks16],
-                                                            dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i % (kAhead + 1)], dsb[ks16],
-                                                            dkacc[db], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * kAhead, 1);
+    for (int i = 0; i < kN / 2; ++i) dvdk(i);
+    pds(std::integral_constant<int, 1>(), lv, dl);
 #pragma unroll
-      for (int i = 0; i < kN; ++i) {
-        if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    for (int i = kN / 2; i < kN; ++i) dvdk(i);
+
+    // schedule (one stream): block 0's S/dP; its LSE/D reads and block 1's
+    // S/dP with block 0's P/dS arithmetic between the MFMAs; block 1's LSE/D
+    // and the first transposed reads, then the products of 16-query steps 0-1
+    // with block 1's P/dS arithmetic between them; then steps 2-3
+    constexpr int kValu = kMask ? 8 : 5;   // vector instructions per MFMA slot
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int t = 0; t < G::kKSteps; ++t) {
+      if (t + 2 < G::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4, 0);
+#pragma unroll
+    for (int t = 0; t < G::kKSteps; ++t) {
+      if (t + 2 < G::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4 * kAheadT, 0);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      if (i + kAheadT < kN) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if (i < kN / 2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
   };
@@ -379,7 +413,16 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     // a wave whose first key no query of the tile sees has nothing to add
-    if (!kCausal || jt * kTileRows + kTileRows - 1 + causal_off >= kw0) compute(jt, stage_tag);
+    if (!kCausal || jt * kTileRows + kTileRows - 1 + causal_off >= kw0) {
+      // causal: the masked form only on tiles that need it. The non-causal
+      // kernel keeps one form (the masked one, whose extra vector work is
+      // interleaved under the MFMAs): with both, its registers overflow.
+      const int q0 = jt * kTileRows;
+      if (!kCausal || (q0 + kTileRows > w.sq) || kw0 + 31 > q0 + causal_off)
+        compute(jt, stage_tag, std::true_type());
+      else
+        compute(jt, stage_tag, std::false_type());
+    }
     lds_barrier();
   };
   if (t0 < n_qt) copy_tile(t0, std::integral_constant<int, 0>());
