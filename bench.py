@@ -8,8 +8,9 @@ varlen-causal d=128 case the headline figure is quoted on: 32768 tokens in 8
 documents (cu_seqlens = round(linspace(0, 32768, 9))), 32 heads, seed 0.
 
 Timing follows the FA4 spill issue's protocol (W warm-up steps, then K timed
-steps; GPU events on the stream the kernel runs on). The defaults (30 warm-up,
-100 timed steps) let the GPU clock settle first: the first tens of
+steps; GPU events on the stream the kernel runs on). The defaults (100 timed
+steps; warm-up steps for about 0.1 s of estimated work, at least 30, e.g. 91
+for c4 and 728 for c3) let the GPU clock settle first: the first tens of
 milliseconds after idle run at lower clocks. value = counted FLOP of
 K steps / elapsed time, with FLOP = 4*h*sum(sq*sk)*d halved for causal.
 
@@ -44,6 +45,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -90,9 +92,12 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     # the GPU's clock ramps up over the first tens of milliseconds of work: the
-    # defaults warm up for about 30 ms of c4 and time about 100 ms
+    # default warm-up covers about 0.1 s of work, and the timed steps about
+    # 100 ms of c4
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=30)
+    # default: at least 30 steps and about 0.1 s of estimated work (at 1 PFLOP/s
+    # counted), so that the clock has settled also for the short workloads
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c4",
                     choices=sorted(SHORT) + sorted(SHORT.values()) +
                     ["x_varlen_noncausal_32k", "x_short_q_long_k", "x_causal_fp4pv_32k"])
@@ -495,6 +500,10 @@ def main():
         if args.splits is not None or args.trace or args.variant != "auto":
             raise SystemExit("--step bwd/fwd_bwd runs the default forward variant, unsplit")
         step = make_bwd_step(w, d, with_fwd=args.step == "fwd_bwd")
+    if args.warmup is None:
+        est_s = (w.flops() * (3.5 if args.step == "fwd_bwd" else 2.5 if args.step == "bwd"
+                              else 1.0)) / 1e15
+        args.warmup = max(30, min(5000, int(math.ceil(0.1 / max(est_s, 1e-9)))))
     if args.counters:
         run_counters(w, d, step)
         return
