@@ -194,9 +194,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBwdWaves * 64, kBwdWaves 
                           amdgpu_waves_per_eu(1, 1)))
 void fmha_bwd_dkdv_kernel(BwdParams p) {
   using G = TileGeom<kD>;
-  __shared__ __attribute__((aligned(1024))) char smem_q[2][G::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char smem_do[2][G::kTileBytes];
-  __shared__ __attribute__((aligned(16))) float smem_rows[2][2 * kTileRows];  // LSE*log2e, D
+  // a ring of three stages: one barrier per tile (see the tile loop)
+  __shared__ __attribute__((aligned(1024))) char smem_q[3][G::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_do[3][G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) float smem_rows[3][2 * kTileRows];  // LSE*log2e, D
 
   const BwdItem w = decode_bwd_item(p, xcd_item(p.batch * p.heads * p.n_blocks), false);
   const int n0 = w.block * kBwdRows;
@@ -401,17 +402,17 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // double-buffered tile loop: tile jt lives in stage (jt - t0) & 1
+  // Tile loop over a ring of three stages: tile jt lives in stage (jt - t0) % 3.
+  // Step jt waits for its own copies of tile jt (issued two steps earlier; only
+  // those of tile jt+1 may still be outstanding), and one barrier then makes
+  // tile jt visible and shows that every wave has finished step jt-1, so the
+  // copies of tile jt+2 may overwrite the stage tile jt-1 used.
   auto step = [&](int jt, auto stage_tag) {
     constexpr int st = decltype(stage_tag)::value;
-    if (jt + 1 < n_qt) {
-      copy_tile(jt + 1, std::integral_constant<int, st ^ 1>());
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kOps));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
+    if (jt + 1 < n_qt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kOps));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    if (jt + 2 < n_qt) copy_tile(jt + 2, std::integral_constant<int, (st + 2) % 3>());
     // a wave whose first key no query of the tile sees has nothing to add
     if (!kCausal || jt * kTileRows + kTileRows - 1 + causal_off >= kw0) {
       // causal: the masked form only on tiles that need it. The non-causal
@@ -423,15 +424,17 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
       else
         compute(jt, stage_tag, std::false_type());
     }
-    lds_barrier();
   };
   if (t0 < n_qt) copy_tile(t0, std::integral_constant<int, 0>());
+  if (t0 + 1 < n_qt) copy_tile(t0 + 1, std::integral_constant<int, 1>());
   int jt = t0;
-  for (; jt + 2 <= n_qt; jt += 2) {
+  for (; jt + 3 <= n_qt; jt += 3) {
     step(jt, std::integral_constant<int, 0>());
     step(jt + 1, std::integral_constant<int, 1>());
+    step(jt + 2, std::integral_constant<int, 2>());
   }
   if (jt < n_qt) step(jt, std::integral_constant<int, 0>());
+  if (jt + 1 < n_qt) step(jt + 1, std::integral_constant<int, 1>());
 
   // dV = sum P^T dO, dK = tau sum dS^T Q for this lane's key
   const int key = kw0 + col;
