@@ -88,6 +88,21 @@ def kernel_template_name(w, variant, split=False):
             f"{str(split).lower()}>")
 
 
+def timed_kernel_resources(w, variant, split=False):
+    """The compiler's resource report entry of the timed forward kernel (None if
+    the report written by the build is missing)."""
+    from head_attention_forward_fmha_amd import build as fb
+    return fb.kernel_resources(fb.mangled_kernel_name(variant, w.head_dim, w.causal,
+                                                      pv_format(w), split))
+
+
+def bwd_kernel_resources(w):
+    """Resource report entries of the three backward kernels, by role."""
+    from head_attention_forward_fmha_amd import build as fb
+    return {role: fb.kernel_resources(fb.mangled_kernel_name(fam, w.head_dim, w.causal))
+            for role, fam in (("prep", "bwd_prep"), ("dkdv", "bwd_dkdv"), ("dq", "bwd_dq"))}
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +442,7 @@ def bwd_line(w, args, inp, d, step, total_ms, each):
                    "causal": w.causal, "seed": w.seed, "step": args.step,
                    "kernel_variant": fm.auto_variant(w.batch, w.max_seqlen_q, w.heads)},
         "roofline": roof,
+        "kernel_resources": bwd_kernel_resources(w),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -559,6 +575,7 @@ def main():
                    "causal": w.causal, "seed": w.seed, "fp8_pv": w.fp8_pv, "fp4_pv": w.fp4_pv,
                    "kernel_variant": variant, "key_splits": d.get("splits", 1)},
         "roofline": roof,
+        "kernel_resources": timed_kernel_resources(w, variant, "splits" in d),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

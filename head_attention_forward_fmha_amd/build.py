@@ -90,6 +90,58 @@ def check_resources(kernels: dict) -> list:
     return bad
 
 
+# kernel families -> the Itanium-mangled prefix of their template instances
+_MANGLED_PREFIX = {
+    "pingpong": "_ZN4fmha24fmha_fwd_pingpong_kernel",
+    "four_wave": "_ZN4fmha15fmha_fwd_kernel",
+    "pipelined": "_ZN4fmha20fmha_fwd_pipe_kernel",
+    "bwd_prep": "_ZN4fmha12_GLOBAL__N_120fmha_bwd_prep_kernel",
+    "bwd_dkdv": "_ZN4fmha12_GLOBAL__N_120fmha_bwd_dkdv_kernel",
+    "bwd_dq": "_ZN4fmha12_GLOBAL__N_118fmha_bwd_dq_kernel",
+}
+
+
+def mangled_kernel_name(family: str, head_dim: int, causal: bool = False, pv: int = 0,
+                        split: bool = False) -> str:
+    """The symbol of one kernel instance, as the resource report names it.
+
+    Template arguments: head dim, causal, P.V format (0 bf16, 1 fp8, 2 fp4) and
+    key split for the forward kernels; the ping-pong's untraced instance."""
+    b = lambda v: "ELb1" if v else "ELb0"  # noqa: E731
+    pre = _MANGLED_PREFIX[family]
+    if family == "pingpong":
+        return (f"{pre}ILi{head_dim}{b(causal)}ELi{pv}{b(split)}ENS_12NoPhaseTraceEEEvNS_9FwdParamsE")
+    if family == "four_wave":
+        return f"{pre}ILi{head_dim}{b(causal)}ELi{pv}{b(split)}EEEvNS_9FwdParamsE"
+    if family == "pipelined":
+        return f"{pre}ILi{head_dim}{b(causal)}EEEvNS_9FwdParamsE"
+    if family == "bwd_prep":
+        return f"{pre}ILi{head_dim}EEEvNS_9BwdParamsE"
+    return f"{pre}ILi{head_dim}{b(causal)}EEEvNS_9BwdParamsE"
+
+
+def kernel_resources(symbol: str, report_path: str = RESOURCE_REPORT):
+    """Registers, scratch, spills, occupancy and LDS of one kernel from the saved
+    resource report, or None when the report or the kernel is missing."""
+    if not os.path.exists(report_path):
+        return None
+    with open(report_path) as f:
+        entry = parse_resource_report(f.read()).get(symbol)
+    if entry is None:
+        return None
+
+    def num(key):
+        v = entry.get(key)
+        return int(v) if v is not None and v.isdigit() else None
+
+    return {"symbol": symbol, "vgprs": num("VGPRs"), "agprs": num("AGPRs"),
+            "sgprs": num("TotalSGPRs"),
+            "scratch_bytes_per_lane": num("ScratchSize [bytes/lane]"),
+            "vgpr_spill": num("VGPRs Spill"), "sgpr_spill": num("SGPRs Spill"),
+            "occupancy_waves_per_simd": num("Occupancy [waves/SIMD]"),
+            "lds_bytes_per_block": num("LDS Size [bytes/block]")}
+
+
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     build_dir = os.path.join(PKG_DIR, "_build")
