@@ -499,7 +499,6 @@ void fmha_bwd_dq_kernel(BwdParams p) {
   int kend = w.sk;
   if (kCausal) kend = min(w.sk, max(0, m0 + kBwdRows + causal_off));
   const int n = (kend + kTileRows - 1) / kTileRows;
-  constexpr int kOps = 2 * G::kLoads;
 
   auto compute = [&](int j, auto stage_tag) {
     constexpr int st = decltype(stage_tag)::value;
@@ -578,20 +577,20 @@ void fmha_bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // One barrier per tile: once this wave's copies of tile j have landed and its
+  // LDS reads of tile j-1 have returned, the barrier makes tile j visible to
+  // every wave and frees tile j-1's stage, which the copies of tile j+1 then
+  // fill while tile j is computed.
   auto step = [&](int j, auto stage_tag) {
     constexpr int st = decltype(stage_tag)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
     if (j + 1 < n) {
       tl.template copy<(st ^ 1) * G::kTileBytes>(k_lds0, k_rsrc, (j + 1) * kTileRows, stride);
       tl.template copy<(st ^ 1) * G::kTileBytes>(v_lds0, v_rsrc, (j + 1) * kTileRows, stride);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kOps));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
     // tiles entirely above the diagonal for all 32 rows of this wave are skipped
     if (!kCausal || j * kTileRows <= wave_q0 + 31 + causal_off) compute(j, stage_tag);
-    lds_barrier();
   };
   if (n > 0) {
     tl.template copy<0>(k_lds0, k_rsrc, 0, stride);
