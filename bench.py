@@ -97,10 +97,10 @@ def timed_kernel_resources(w, variant, split=False):
 
 
 def bwd_kernel_resources(w):
-    """Resource report entries of the three backward kernels, by role."""
+    """Resource report entries of the two backward kernels, by role."""
     from head_attention_forward_fmha_amd import build as fb
     return {role: fb.kernel_resources(fb.mangled_kernel_name(fam, w.head_dim, w.causal))
-            for role, fam in (("prep", "bwd_prep"), ("dkdv", "bwd_dkdv"), ("dq", "bwd_dq"))}
+            for role, fam in (("dq", "bwd_dq"), ("dkdv", "bwd_dkdv"))}
 
 
 def parse_args():
@@ -424,9 +424,9 @@ def bwd_line(w, args, inp, d, step, total_ms, each):
     peak = MI355X_PEAK_TFLOPS["bf16"]
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": None,
-            "kernel": f"fmha_bwd call: fmha::fmha_bwd_prep_kernel<{w.head_dim}>, "
-                      f"fmha::fmha_bwd_dkdv_kernel<{w.head_dim}, {str(w.causal).lower()}>, "
-                      f"fmha::fmha_bwd_dq_kernel<{w.head_dim}, {str(w.causal).lower()}>",
+            "kernel": f"fmha_bwd call: fmha::fmha_bwd_dq_kernel<{w.head_dim}, "
+                      f"{str(w.causal).lower()}>, "
+                      f"fmha::fmha_bwd_dkdv_kernel<{w.head_dim}, {str(w.causal).lower()}>",
             "launch_avg_us": round(bwd_ms * 1e3, 2),
             "algorithmic_flop_per_launch": 2.5 * w.flops()}
     line = {

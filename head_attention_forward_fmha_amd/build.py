@@ -95,7 +95,6 @@ _MANGLED_PREFIX = {
     "pingpong": "_ZN4fmha24fmha_fwd_pingpong_kernel",
     "four_wave": "_ZN4fmha15fmha_fwd_kernel",
     "pipelined": "_ZN4fmha20fmha_fwd_pipe_kernel",
-    "bwd_prep": "_ZN4fmha12_GLOBAL__N_120fmha_bwd_prep_kernel",
     "bwd_dkdv": "_ZN4fmha12_GLOBAL__N_120fmha_bwd_dkdv_kernel",
     "bwd_dq": "_ZN4fmha12_GLOBAL__N_118fmha_bwd_dq_kernel",
 }
@@ -115,8 +114,6 @@ def mangled_kernel_name(family: str, head_dim: int, causal: bool = False, pv: in
         return f"{pre}ILi{head_dim}{b(causal)}ELi{pv}{b(split)}EEEvNS_9FwdParamsE"
     if family == "pipelined":
         return f"{pre}ILi{head_dim}{b(causal)}EEEvNS_9FwdParamsE"
-    if family == "bwd_prep":
-        return f"{pre}ILi{head_dim}EEEvNS_9BwdParamsE"
     return f"{pre}ILi{head_dim}{b(causal)}EEEvNS_9BwdParamsE"
 
 

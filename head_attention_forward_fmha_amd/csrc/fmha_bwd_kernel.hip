@@ -9,19 +9,21 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),   D_i = dO_i . O_i,
 //   dQ = tau dS K, dK = tau dS^T Q.
 //
-// (D_i equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j.) Three launches:
+// (D_i equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j.) Two launches:
 //
-//   1. preprocessing: D and LSE * log2(e) per (row, head), HBM-bound;
+//   1. dQ: a workgroup owns 128 queries, 32 per wave, with Q and dO in
+//      registers, and streams 64-key K and V tiles: S^T = K Q^T and
+//      dP^T = V dO^T by rows, dQ^T += K^T dS^T transposed. Holding each
+//      query's dO row, it also computes D and LSE * log2(e) per (row, head)
+//      and writes them to the workspace;
 //   2. dK/dV: a workgroup owns 128 keys of one (document, head), 32 per wave,
 //      with K and V held in registers, and streams the document's 64-row Q and
-//      dO tiles through double-buffered LDS. It is the forward's structure with
+//      dO tiles through a three-stage LDS ring. It is the forward's structure with
 //      the roles of queries and keys swapped: S = Q K^T and dP = dO V^T read the
 //      streamed tiles by rows (lane = key, registers = queries), and
 //      dV^T += dO^T P and dK^T += Q^T dS read them transposed (ds_read_b64_tr_b16),
 //      with P and dS as the register operand, exactly as O^T += V^T P^T;
-//   3. dQ: a workgroup owns 128 queries, 32 per wave, with Q and dO in
-//      registers, and streams 64-key K and V tiles: S^T = K Q^T and
-//      dP^T = V dO^T by rows, dQ^T += K^T dS^T transposed.
+//      it reads D and LSE * log2(e) of each query tile from the workspace.
 //
 // Every output element is written by exactly one lane with a fixed summation
 // order, so the result is deterministic (no atomics); the price is that S and dP
@@ -159,35 +161,7 @@ __device__ __forceinline__ void store_bf16_rows(bf16_t* row, const f32x16* acc, 
     }
 }
 
-// ---------------------------------------------------------------- 1. preprocessing
-
-// D = dO . O and LSE * log2(e) per (row, head). A row of kD bf16 is spread over
-// kD/8 lanes (16-byte loads) and reduced with cross-lane shuffles.
-template <int kD>
-__global__ __launch_bounds__(256) void fmha_bwd_prep_kernel(BwdParams p) {
-  constexpr int kLanesPerRow = kD / 8;
-  const long long n_rows = (long long)p.total_q * p.heads;
-  const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / kLanesPerRow;
-  const int sub = threadIdx.x % kLanesPerRow;
-  if (row >= n_rows) return;
-  const int t = (int)(row / p.heads);
-  const int h = (int)(row - (long long)t * p.heads);
-  const bf16x8 a = *((const bf16x8*)p.dout + row * kLanesPerRow + sub);
-  const bf16x8 b = *((const bf16x8*)p.out + row * kLanesPerRow + sub);
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
-#pragma unroll
-  for (int m = 1; m < kLanesPerRow; m *= 2) s += __shfl_xor(s, m);
-  if (sub == 0) {
-    const size_t idx = (size_t)h * p.total_q + t;
-    p.delta[idx] = s;
-    const float l = p.lse[idx];
-    p.lse2[idx] = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2eF;
-  }
-}
-
-// ---------------------------------------------------------------- 2. dK and dV
+// ---------------------------------------------------------------- dK and dV
 
 template <int kD, bool kCausal>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdWaves * 64, kBwdWaves * 64),
@@ -445,7 +419,7 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-// ---------------------------------------------------------------- 3. dQ
+// ---------------------------------------------------------------- dQ
 
 template <int kD, bool kCausal>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdWaves * 64, kBwdWaves * 64),
@@ -479,8 +453,42 @@ void fmha_bwd_dq_kernel(BwdParams p) {
       doreg[t] = *(const bf16x8*)((const bf16_t*)p.dout + off + 16 * t);
     }
   }
-  const float lse2 = p.lse2[(size_t)w.head * p.total_q + qrow];
-  const float delta = p.delta[(size_t)w.head * p.total_q + qrow];
+  // LSE*log2e and D = dO . O of this lane's query. D is summed like a tree over
+  // 16-byte chunks of the row: each chunk sequentially, then pairs of chunks;
+  // lane half h holds chunks 2t + h, so the halves first add each other's chunk
+  // sums. The workgroup that owns a query writes both for the dK/dV kernel,
+  // which runs after this one.
+  const size_t row_idx = (size_t)w.head * p.total_q + qrow;
+  const float lse_nat = p.lse[row_idx];
+  const float lse2 = (lse_nat == -__builtin_inff()) ? __builtin_inff() : lse_nat * kLog2eF;
+  float delta;
+  {
+    const size_t off = (size_t)qrow * p.heads * kD + (size_t)w.head * kD + 8 * half;
+    float part[G::kKSteps];
+#pragma unroll
+    for (int t = 0; t < G::kKSteps; ++t) {
+      const bf16x8 o = *(const bf16x8*)((const bf16_t*)p.out + off + 16 * t);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)doreg[t][e] * (float)o[e];
+      part[t] = acc;
+    }
+#pragma unroll
+    for (int t = 0; t < G::kKSteps; ++t) part[t] += __shfl_xor(part[t], 32);
+#pragma unroll
+    for (int m = 1; m < G::kKSteps; m *= 2) {
+      float sum[G::kKSteps];
+#pragma unroll
+      for (int t = 0; t < G::kKSteps; ++t) sum[t] = part[t] + part[t ^ m];
+#pragma unroll
+      for (int t = 0; t < G::kKSteps; ++t) part[t] = sum[t];
+    }
+    delta = part[0];
+  }
+  if (half == 0 && qi < w.sq) {
+    p.delta[row_idx] = delta;
+    p.lse2[row_idx] = lse2;
+  }
   f32x16 dqacc[G::kDBlocks];
 #pragma unroll
   for (int db = 0; db < G::kDBlocks; ++db)
@@ -612,24 +620,18 @@ void fmha_bwd_dq_kernel(BwdParams p) {
 template <int kD, bool kCausal>
 hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t stream) {
   BwdParams p = p0;
-  const long long n_rows = (long long)p.total_q * p.heads;
-  if (n_rows > 0) {
-    const long long rows_per_block = 256 / (kD / 8);
-    hipLaunchKernelGGL(fmha_bwd_prep_kernel<kD>,
-                       dim3((unsigned)((n_rows + rows_per_block - 1) / rows_per_block)), dim3(256),
-                       0, stream, p);
-  }
-  p.n_blocks = (p.max_seqlen_k + kBwdRows - 1) / kBwdRows;
+  // dQ first: its workgroups also write D and LSE*log2e, which dK/dV reads
+  p.n_blocks = (p.max_seqlen_q + kBwdRows - 1) / kBwdRows;
   long long items = (long long)p.batch * p.heads * p.n_blocks;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   if (items > 0)
-    hipLaunchKernelGGL((fmha_bwd_dkdv_kernel<kD, kCausal>), dim3((unsigned)items),
+    hipLaunchKernelGGL((fmha_bwd_dq_kernel<kD, kCausal>), dim3((unsigned)items),
                        dim3(kBwdWaves * 64), 0, stream, p);
-  p.n_blocks = (p.max_seqlen_q + kBwdRows - 1) / kBwdRows;
+  p.n_blocks = (p.max_seqlen_k + kBwdRows - 1) / kBwdRows;
   items = (long long)p.batch * p.heads * p.n_blocks;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   if (items > 0)
-    hipLaunchKernelGGL((fmha_bwd_dq_kernel<kD, kCausal>), dim3((unsigned)items),
+    hipLaunchKernelGGL((fmha_bwd_dkdv_kernel<kD, kCausal>), dim3((unsigned)items),
                        dim3(kBwdWaves * 64), 0, stream, p);
   return hipGetLastError();
 }

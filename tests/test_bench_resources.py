@@ -60,7 +60,7 @@ def test_backward_kernels_are_in_the_report(causal):
     w = WORKLOADS["c4_varlen_causal_32k"]
     w = dataclasses.replace(w, causal=causal)
     res = _bench().bwd_kernel_resources(w)
-    assert sorted(res) == ["dkdv", "dq", "prep"]
+    assert sorted(res) == ["dkdv", "dq"]
     for entry in res.values():
         _clean(entry)
 
