@@ -118,10 +118,25 @@ struct BwdItem {
   int head, q_start, k_start, sq, sk, block;
 };
 
+// Items are numbered through groups of (document, head) pairs, about
+// kGroupItems items each, and within a group block by block: a group's longest
+// blocks start first, its shortest are dispatched last, and the Q/dO or K/V rows
+// that its concurrent workgroups stream are those of a few pairs only. About
+// two items per CU of an XCD measured best (fewer pairs per group leave a
+// longer tail, more pairs spread the rows over more of the L2). Without a
+// causal mask all blocks of a document cost the same, and the items stay in
+// pair-major order (one group per pair).
+constexpr int kGroupItems = 64;
+
 __device__ __forceinline__ BwdItem decode_bwd_item(const BwdParams& p, int item,
-                                                   bool reverse_blocks) {
-  const int pair = item / p.n_blocks;
-  const int b = item - pair * p.n_blocks;
+                                                   bool reverse_blocks, bool grouped) {
+  const int n_pairs = p.batch * p.heads;
+  const int group_pairs = grouped ? max(1, kGroupItems / p.n_blocks) : 1;
+  const int base = item / (group_pairs * p.n_blocks) * group_pairs;
+  const int g = min(group_pairs, n_pairs - base);   // pairs in this group
+  const int r = item - base * p.n_blocks;
+  const int b = r / g;
+  const int pair = base + (r - b * g);
   BwdItem w;
   w.block = reverse_blocks ? p.n_blocks - 1 - b : b;
   const int doc = pair / p.heads;
@@ -173,7 +188,7 @@ void fmha_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_do[3][G::kTileBytes];
   __shared__ __attribute__((aligned(16))) float smem_rows[3][2 * kTileRows];  // LSE*log2e, D
 
-  const BwdItem w = decode_bwd_item(p, xcd_item(p.batch * p.heads * p.n_blocks), false);
+  const BwdItem w = decode_bwd_item(p, xcd_item(p.batch * p.heads * p.n_blocks), false, kCausal);
   const int n0 = w.block * kBwdRows;
   if (n0 >= w.sk) return;   // uniform over the workgroup
   const int wave = threadIdx.x >> 6;
@@ -430,7 +445,7 @@ void fmha_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_v[2][G::kTileBytes];
 
   // causal: the longest query blocks (most keys) first
-  const BwdItem w = decode_bwd_item(p, xcd_item(p.batch * p.heads * p.n_blocks), kCausal);
+  const BwdItem w = decode_bwd_item(p, xcd_item(p.batch * p.heads * p.n_blocks), kCausal, kCausal);
   const int m0 = w.block * kBwdRows;
   if (m0 >= w.sq) return;   // uniform over the workgroup
   const int wave = threadIdx.x >> 6;
