@@ -8,10 +8,11 @@
 
 namespace fmha {
 
-// Backward pass. D_i = dO_i . O_i and LSE_i * log2(e) (+inf for a row that saw
-// no key, so that its P is 0) are computed once per row by the preprocessing
-// kernel; the dK/dV kernel walks query tiles per key block and the dQ kernel
-// key tiles per query block, each recomputing P from the saved LSE.
+// Backward pass. The dQ kernel walks key tiles per query block and also
+// computes D_i = dO_i . O_i and LSE_i * log2(e) (+inf for a row that saw no
+// key, so that its P is 0) once per row, into the workspace; the dK/dV kernel,
+// launched after it, walks query tiles per key block and reads them. Both
+// recompute P from the saved LSE.
 struct BwdParams {
   const void* q;          // bf16 [total_q, heads, d]
   const void* k;          // bf16 [total_k, heads, d]
