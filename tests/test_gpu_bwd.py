@@ -110,6 +110,13 @@ def test_bwd_ragged_and_empty(lens, causal, d):
     _parity(lens, 3, d, causal, seed=len(lens) + d)
 
 
+def test_bwd_long_causal_document_one_pair_per_item_group():
+    """Causal items are dispatched in groups of about 64: a document of 8300
+    tokens has 65 blocks of 128 rows, so its groups hold one (document, head)
+    pair each, while the short second document's pairs share groups."""
+    _parity(((8300, 8300), (300, 300)), 2, 64, True)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_isolated_from_the_forward(causal):
     """The backward alone, given the oracle's O and LSE."""
