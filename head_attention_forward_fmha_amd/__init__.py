@@ -62,7 +62,11 @@ def _prepare(q, k, v_like, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
     import torch
     if q.dim() == 4:
         b, sq, h, d = q.shape
+        if k.dim() != 4 or v_like.dim() != 4:
+            raise ValueError("dense q [b, s, h, d] needs dense k and v")
         sk = k.shape[1]
+        if k.shape[0] != b or v_like.shape[0] != b or v_like.shape[1] != sk:
+            raise ValueError("dense k and v must have q's batch and the same sequence length")
         if cu_seqlens_q is not None or cu_seqlens_k is not None:
             raise ValueError("dense [b, s, h, d] inputs take no cu_seqlens")
         return dict(batch=b, total_q=b * sq, total_k=b * sk, max_q=sq, max_k=sk, heads=h, d=d,
@@ -71,6 +75,8 @@ def _prepare(q, k, v_like, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
         raise ValueError("q must be [total, heads, d] or [b, s, heads, d]")
     tq, h, d = q.shape
     tk = k.shape[0]
+    if k.dim() != 3 or v_like.dim() != 3 or v_like.shape[0] != tk:
+        raise ValueError("packed k and v must be [total_k, heads, d] with the same total_k")
     if cu_seqlens_q is None:
         if cu_seqlens_k is not None:
             raise ValueError("cu_seqlens_q and cu_seqlens_k must be given together")
@@ -88,6 +94,26 @@ def _prepare(q, k, v_like, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
     return dict(batch=cu_seqlens_q.numel() - 1, total_q=tq, total_k=tk, max_q=int(max_seqlen_q),
                 max_k=int(max_seqlen_k), heads=h, d=d, cu_q=cu_seqlens_q, cu_k=cu_seqlens_k,
                 out_shape=(tq, h, d), lse_len=tq)
+
+
+def _outputs(s, out, lse, return_lse, device):
+    """The caller's out / lse (checked against the problem), or new ones."""
+    import torch
+    if out is None:
+        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=device)
+    else:
+        _check_tensor("out", out, torch.bfloat16, len(s["out_shape"]), device)
+        if tuple(out.shape) != tuple(s["out_shape"]):
+            raise ValueError(f"out must have shape {tuple(s['out_shape'])}, got {tuple(out.shape)}")
+    if lse is None:
+        if return_lse:
+            lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=device)
+    else:
+        _check_tensor("lse", lse, torch.float32, 2, device)
+        if tuple(lse.shape) != (s["heads"], s["lse_len"]):
+            raise ValueError(f"lse must have shape {(s['heads'], s['lse_len'])}, "
+                             f"got {tuple(lse.shape)}")
+    return out, lse
 
 
 def _stream_handle(device) -> int:
@@ -115,10 +141,7 @@ def fwd(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[in
     if k.shape != v.shape or k.shape[-2:] != q.shape[-2:]:
         raise ValueError("k and v must match, with q's heads and head_dim")
     scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
-    if out is None:
-        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    out, lse = _outputs(s, out, lse, return_lse, dev)
     st = lib.fmha_fwd_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(s["cu_q"]), _ptr(s["cu_k"]),
                               s["batch"], s["total_q"], s["total_k"], s["max_q"], s["max_k"],
                               s["heads"], s["d"], int(bool(causal)), ctypes.c_float(scale),
@@ -145,10 +168,7 @@ def fwd_fp8pv(q, k, v_e4m3, v_scale, cu_seqlens_q=None, cu_seqlens_k=None,
     if k.shape != v_e4m3.shape or k.shape[-2:] != q.shape[-2:] or v_scale.numel() != s["heads"]:
         raise ValueError("k, v_e4m3, v_scale shapes do not match q")
     scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
-    if out is None:
-        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    out, lse = _outputs(s, out, lse, return_lse, dev)
     st = lib.fmha_fwd_fp8pv_variant(_ptr(q), _ptr(k), _ptr(v_e4m3), _ptr(v_scale),
                                     _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"], s["total_q"],
                                     s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"],
@@ -183,10 +203,7 @@ def fwd_fp4pv(q, k, v_e2m1, v_mx_scale, cu_seqlens_q=None, cu_seqlens_k=None,
             or tuple(v_mx_scale.shape) != ((tk + 31) // 32, h, d)):
         raise ValueError("k, v_e2m1, v_mx_scale shapes do not match q")
     scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
-    if out is None:
-        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    out, lse = _outputs(s, out, lse, return_lse, dev)
     st = lib.fmha_fwd_fp4pv_variant(_ptr(q), _ptr(k), _ptr(v_e2m1), _ptr(v_mx_scale),
                                     _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"], s["total_q"],
                                     s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"],
@@ -246,10 +263,7 @@ def fwd_splitkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None,
     if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if out is None:
-        out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((s["heads"], s["lse_len"]), dtype=torch.float32, device=dev)
+    out, lse = _outputs(s, out, lse, return_lse, dev)
     st = lib.fmha_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(s["cu_q"]), _ptr(s["cu_k"]),
                               s["batch"], s["total_q"], s["total_k"], s["max_q"], s["max_k"],
                               s["heads"], s["d"], int(bool(causal)), ctypes.c_float(scale),
@@ -323,10 +337,7 @@ def merge_partials(o_part, lse_part, out=None, lse=None, return_lse: bool = True
     n_parts, tq, h, d = o_part.shape
     if tuple(lse_part.shape) != (n_parts, h, tq):
         raise ValueError("lse_part must be [S, heads, total_q] matching o_part")
-    if out is None:
-        out = torch.empty((tq, h, d), dtype=torch.bfloat16, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((h, tq), dtype=torch.float32, device=dev)
+    out, lse = _outputs(dict(out_shape=(tq, h, d), heads=h, lse_len=tq), out, lse, return_lse, dev)
     st = lib.fmha_merge_partials(_ptr(o_part), _ptr(lse_part), n_parts, tq, h, d, _ptr(out),
                                  _ptr(lse), ctypes.c_void_p(_stream_handle(dev)))
     if st != FMHA_OK:
@@ -356,9 +367,26 @@ def fwd_trace(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen
     if pv not in _PV_FORMATS:
         raise ValueError(f"pv must be one of {sorted(_PV_FORMATS)}")
     _check_tensor("v", v, torch.bfloat16 if pv == "bf16" else torch.uint8, 3, dev)
-    if pv != "bf16":
-        _check_tensor("v_scale", v_scale, torch.float32 if pv == "e4m3" else torch.uint8,
-                      v_scale.dim(), dev)
+    tk, h, d = k.shape
+    if q.shape[1:] != k.shape[1:]:
+        raise ValueError("k must have q's heads and head_dim")
+    if pv == "e2m1":
+        if tuple(v.shape) != (tk, h, d // 2):
+            raise ValueError("e2m1 v must be [total_k, heads, head_dim / 2]")
+        if v_scale is None:
+            raise ValueError("e2m1 v needs its E8M0 exponents (v_scale)")
+        _check_tensor("v_scale", v_scale, torch.uint8, 3, dev)
+        if tuple(v_scale.shape) != ((tk + 31) // 32, h, d):
+            raise ValueError("e2m1 v_scale must be [ceil(total_k / 32), heads, head_dim]")
+    else:
+        if tuple(v.shape) != (tk, h, d):
+            raise ValueError("v must have k's shape")
+        if pv == "e4m3":
+            if v_scale is None:
+                raise ValueError("e4m3 v needs its per-head scale (v_scale)")
+            _check_tensor("v_scale", v_scale, torch.float32, 1, dev)
+            if v_scale.numel() != h:
+                raise ValueError("e4m3 v_scale must be [heads]")
     s = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
     out = torch.empty(s["out_shape"], dtype=torch.bfloat16, device=dev)
