@@ -33,7 +33,8 @@ and dP). The roofline object then brackets the whole fmha_bwd call (its three
 launches, on one stream); rocprofv3 summaries give the per-kernel split.
 
 Options: --workload c1|c2|c3|c4|c5 (other workloads, for measurement only:
-x_varlen_noncausal_32k, x_short_q_long_k, x_causal_fp4pv_32k), --splits N|auto
+x_varlen_noncausal_32k, x_short_q_long_k, x_causal_fp4pv_32k, x_causal_bf16_32k),
+--splits N|auto
 (the split-KV pass), --trace coarse|detailed (pipeline summary of a traced launch),
 --variant, --no-cpu-baseline, --counters (a short run for rocprofv3 --pmc: a
 copy kernel of known size, then a few steps), --summarize-counters and
@@ -115,7 +116,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c4",
                     choices=sorted(SHORT) + sorted(SHORT.values()) +
-                    ["x_varlen_noncausal_32k", "x_short_q_long_k", "x_causal_fp4pv_32k"])
+                    ["x_varlen_noncausal_32k", "x_short_q_long_k", "x_causal_fp4pv_32k",
+                     "x_causal_bf16_32k"])
     ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong", "pipelined"],
                     help="kernel variant (auto picks by problem size)")
     ap.add_argument("--splits", default=None,

@@ -139,37 +139,32 @@ def kernel_resources(symbol: str, report_path: str = RESOURCE_REPORT):
             "lds_bytes_per_block": num("LDS Size [bytes/block]")}
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = _hipcc()
-    build_dir = os.path.join(PKG_DIR, "_build")
-    os.makedirs(build_dir, exist_ok=True)
-    objs = []
-    reports = []
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(build_dir, src + ".o")
-        cmd = [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC,
-               "-Rpass-analysis=kernel-resource-usage", "-c", path, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError(f"hipcc failed on {src}")
-        reports.append(r.stderr)
-        objs.append(obj)
-    # the microbenchmark library: one source, its own shared object
-    obj = os.path.join(build_dir, MICROBENCH_SOURCE + ".o")
-    cmd = [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-Rpass-analysis=kernel-resource-usage", "-c",
-           os.path.join(CSRC, MICROBENCH_SOURCE), "-o", obj]
+def _compile(hipcc: str, src_path: str, obj: str, includes, verbose: bool) -> str:
+    cmd = [hipcc, *HIP_FLAGS, *[a for d in includes for a in ("-I", d)],
+           "-Rpass-analysis=kernel-resource-usage", "-c", src_path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed on {MICROBENCH_SOURCE}")
-    reports.append(r.stderr)
-    mb_obj = obj
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src_path)}")
+    return r.stderr
+
+
+def build(verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = _hipcc()
+    build_dir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    jobs = [(os.path.join(CSRC, src), os.path.join(build_dir, src + ".o"), (INCLUDE, CSRC))
+            for src in SOURCES]
+    # the microbenchmark library: one source, its own shared object
+    mb_obj = os.path.join(build_dir, MICROBENCH_SOURCE + ".o")
+    jobs.append((os.path.join(CSRC, MICROBENCH_SOURCE), mb_obj, (INCLUDE,)))
+    # the sources compile independently; a few at a time keeps memory modest
+    with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as pool:
+        reports = list(pool.map(lambda j: _compile(hipcc, j[0], j[1], j[2], verbose), jobs))
+    objs = [j[1] for j in jobs[:len(SOURCES)]]
     rpaths = [d for d in (_torch_lib_dir(), "/opt/rocm/lib") if d]
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,

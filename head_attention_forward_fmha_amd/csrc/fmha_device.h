@@ -53,9 +53,12 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 64;     // keys per K/V tile
 constexpr int kXcds = 8;    // accelerator complex dies of an MI355X
-// fp8 P.V: P is quantised as e4m3(2^8 * p); 2^8 is the largest power of two
-// not above e4m3's maximum 448, so p = 1 maps exactly and small p stay normal.
-constexpr float kPScaleLog2 = 8.f;
+// fp8 P.V: P is quantised as e4m3(2^(c s - M + 5)) with M an integer running
+// maximum in exp2 units, so a key at the row maximum scales to at most 2^5 and
+// the lazy raise below has a factor 14 of headroom under e4m3's maximum 448;
+// values down to 2^-11 of the maximum stay in e4m3's normal range.
+constexpr float kPScaleLog2 = 5.f;
+constexpr float kE4m3Max = 448.f;
 
 // ---------------------------------------------------------------- primitives
 
@@ -344,8 +347,8 @@ struct WaveTile {
   static constexpr int kDBlocks = kD / 32;               // O^T accumulator blocks
   static constexpr int kKeyBlocks = kBN / 32;            // S^T accumulator blocks
   static constexpr int kVReads = kFp8 ? 1 : 2;
-  // bf16 P tolerates p up to 2^8 (lazy maximum); e4m3 P already spends its
-  // range on the 2^kPScaleLog2 scale, so the fp8 path keeps the exact maximum.
+  // bf16 P tolerates p up to 2^8 (lazy maximum); e4m3 P up to its largest
+  // finite value (kE4m3Max), with the integer maximum of softmax_e4m3.
   static constexpr float kLazyLimit = 256.f;  // 2^8: largest p the bf16 path allows
   static_assert(kLoadsPerWave >= 1 && kLoadsPerWave * kThreads * 16 == kTileBytes,
                 "K tile must split into whole lane loads");
@@ -367,7 +370,7 @@ struct WaveTile {
   i32x4 pb4;             // e2m1 P of the last softmaxed tile (32 keys per lane)
   int p_scale;           // its E8M0 group scale for this lane's 32 keys
   float m_run, l_run, c;
-  float m_log2;          // e2m1 path: integer running maximum in exp2 units
+  float m_log2;          // e4m3 and e2m1 paths: integer running maximum in exp2 units
   int key_lo;            // keys before this are hidden (block-aligned fp4 tiles)
   // per-lane LDS byte offsets of the operand reads within a stage's tile
   int k_off[kKSteps];
@@ -632,7 +635,7 @@ struct WaveTile {
     } else if constexpr (!kFp8) {
       softmax_lazy();
     } else {
-      softmax_exact();
+      softmax_e4m3();
     }
   }
 
@@ -747,21 +750,40 @@ struct WaveTile {
     l_run += lane_sum;
   }
 
-  // e4m3 P: the exact running maximum, so that 2^kPScaleLog2 * p <= 2^8 fits
-  // e4m3's range (max 448) without saturation.
-  __device__ __forceinline__ void softmax_exact() {
-    const float mx = tile_row_max();
-    // NaN when both are -inf (a row with nothing visible yet): no raise
-    const bool raise = mx > m_run;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      // raise implies mx finite; alpha = 0 when m_run = -inf
-      const float alpha = raise ? __builtin_amdgcn_exp2f((m_run - mx) * c) : 1.f;
-      m_run = raise ? mx : m_run;
-      rescale(alpha);
-    }
+  // e4m3 P: an integer running maximum M in exp2 units, raised lazily. The
+  // tile's values x = exp2(fma(s, c, 5 - M)) are rounded to e4m3 and summed
+  // in fp32; M is kept as long as no x exceeds e4m3's largest value, checked
+  // on each lane's partial sum (every x is at most that sum). A row that
+  // exceeds it, or has no maximum yet, takes M = ceil(c * tile row max), so its
+  // x are at most 2^5, and the wave redoes the tile. Every O and l rescale is
+  // then an exact power of two, 2^(M_old - M_new), and because scaling by a
+  // power of two commutes with rounding to e4m3 in its normal range, the
+  // quantised P times 2^(M - 5) is the e4m3-precision rounding of 2^(c s)
+  // whatever M is: P_hat depends on the scores alone (below 2^-6 of the
+  // scale, in e4m3's subnormal range, on M as well).
+  __device__ __forceinline__ void softmax_e4m3() {
     float rs[4];
     exp_sum_convert(rs);
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    float lane_sum = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    // NaN-safe: inf or NaN sums also take the slow path
+    const bool raise = (m_log2 == -__builtin_inff()) || !(lane_sum <= kE4m3Max);
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(raise);
+    if (mask != 0) {
+      const uint32_t rows = (uint32_t)mask | (uint32_t)(mask >> 32);
+      const bool row_raise = (rows >> col) & 1u;
+      // -inf for a row that sees no key yet, which keeps M = -inf
+      const float cand = __builtin_ceilf(tile_row_max() * c);
+      const bool up = row_raise && (cand > m_log2);
+      const float m_new = up ? cand : m_log2;
+      // 2^(M_old - M_new): 1 for rows not raised, 0 for a first maximum (the
+      // clamp also absorbs -inf and the NaN of -inf - -inf, where O = l = 0)
+      const float alpha = __builtin_ldexpf(1.f, (int)fmaxf(m_log2 - m_new, -200.f));
+      m_log2 = m_new;
+      rescale(alpha);
+      exp_sum_convert(rs);
+      lane_sum = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
+    l_run += lane_sum;
   }
 
   // Row maximum of the tile's scores over both lane halves. Four independent
@@ -785,12 +807,14 @@ struct WaveTile {
 
   // p = exp2(fma(s, c, -c*m_run)) for the 32 scores of this lane (the scale and
   // the row maximum folded into one multiply-add), partial row sums of the fp32
-  // p in four chains, and P rounded for the P.V operand (bf16 RNE, or e4m3 with
-  // 2^kPScaleLog2 folded into the exponent). The scores in sacc are kept.
+  // p in four chains, and P rounded for the P.V operand: bf16 RNE, or e4m3 of
+  // exp2(fma(s, c, kPScaleLog2 - M)), the scale and the integer maximum folded
+  // into the addend. The scores in sacc are kept.
   __device__ __forceinline__ void exp_sum_convert(float (&rs)[4]) {
     // an all-masked row keeps the fold finite
-    const float neg_mc = (m_run == -__builtin_inff()) ? 0.f : -m_run * c;
-    const float p_add = kFp8 ? neg_mc + kPScaleLog2 : neg_mc;
+    float p_add;
+    if constexpr (kFp8) p_add = kPScaleLog2 - ((m_log2 == -__builtin_inff()) ? 0.f : m_log2);
+    else p_add = (m_run == -__builtin_inff()) ? 0.f : -m_run * c;
     rs[0] = rs[1] = rs[2] = rs[3] = 0.f;
     if constexpr (!kFp8) {
       static_for<kBN / 16>([&](auto ks_tag) {
@@ -1111,7 +1135,7 @@ struct WaveTile {
     if (p.lse != nullptr && half == 0) {
       float lse = -__builtin_inff();
       const float lsub = kFp8 ? kPScaleLog2 : 0.f;
-      const float mlog2 = kFp4 ? m_log2 : m_run * c;
+      const float mlog2 = (kFp4 || kFp8) ? m_log2 : m_run * c;
       if (l_run > 0.f)
         lse = (mlog2 + (__builtin_amdgcn_logf(l_run) - lsub)) * 0.69314718055994531f;
       p.lse[(size_t)w.head * p.total_q + w.q_start + qi] = lse;

@@ -69,11 +69,12 @@ def loss_grad_mean_square(o) -> np.ndarray:
 _U = 2.0 ** -9   # unit roundoff of bf16 (round to nearest)
 
 
-def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block, want_scale=False):
+def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block, want_scale=False, first_row=0):
     """Gradients for one (document, head): q/do [sq, d], k/v [sk, d] in fp64.
 
     With want_scale, also the rounding scales T(dQ), T(dK), T(dV) (module
-    docstring); their squares are accumulated over row blocks."""
+    docstring); their squares are accumulated over row blocks. Rows before
+    ``first_row`` are skipped (see attention_backward)."""
     sk = kb.shape[0]
     dq = np.zeros_like(qb)
     dk = np.zeros_like(kb)
@@ -81,7 +82,7 @@ def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block, want_scale=False)
     t2q = np.zeros_like(qb)
     t2k = np.zeros_like(kb)
     t2v = np.zeros_like(vb)
-    for r0 in range(0, sq, row_block):
+    for r0 in range(first_row, sq, row_block):
         r1 = min(sq, r0 + row_block)
         rows = np.arange(r0, r1)
         s = scores(qb[r0:r1], kb, tau)
@@ -100,6 +101,14 @@ def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block, want_scale=False)
             t2v += _U * _U * (p2.T @ (dob[r0:r1] ** 2))
             t2q[r0:r1] = tau * tau * (_U * _U * (ds2 @ (kb * kb)) + e2[:, None] * (p @ kb) ** 2)
             t2k += tau * tau * (_U * _U * (ds2.T @ q2) + (p2 * e2[:, None]).T @ q2)
+    if first_row > 0:
+        # the skipped rows' dQ is unknown, and so are dK, dV of every key one of
+        # them sees (causal: keys up to first_row - 1 + sk - sq; otherwise all)
+        last_seen = first_row - 1 + (sk - sq) if causal else sk - 1
+        for x in (dq, t2q):
+            x[:first_row] = np.nan
+        for x in (dk, dv, t2k, t2v):
+            x[:max(0, last_seen + 1)] = np.nan
     if want_scale:
         return dq, dk, dv, np.sqrt(t2q), np.sqrt(t2k), np.sqrt(t2v)
     return dq, dk, dv
@@ -108,13 +117,17 @@ def _backward_one(qb, kb, vb, dob, sq, causal, tau, row_block, want_scale=False)
 def attention_backward(q, k, v, dout, cu_seqlens_q: Sequence[int], cu_seqlens_k: Sequence[int],
                        causal: bool, softmax_scale: float, row_block: int = DEFAULT_ROW_BLOCK,
                        heads: Optional[Iterable[int]] = None,
-                       docs: Optional[Iterable[int]] = None, rounding_scale: bool = False):
+                       docs: Optional[Iterable[int]] = None, rounding_scale: bool = False,
+                       first_row: int = 0):
     """Gradients of packed varlen attention.
 
     q, dout [total_q, h, d]; k, v [total_k, h, d]; any float dtype (widened
     exactly to fp64). Returns (dQ, dK, dV) fp64 in the shapes of q, k, v, and
     with ``rounding_scale`` also their rounding scales (T(dQ), T(dK), T(dV)).
     Rows of documents or heads not selected (``heads``/``docs``) are NaN.
+    ``first_row`` skips each document's first query rows (only the cost of a
+    long document): their dQ, and dK and dV of every key they see, are NaN;
+    everything else is exactly what the full computation gives.
     """
     cq = np.asarray(cu_seqlens_q, dtype=np.int64)
     ck = np.asarray(cu_seqlens_k, dtype=np.int64)
@@ -127,7 +140,8 @@ def attention_backward(q, k, v, dout, cu_seqlens_q: Sequence[int], cu_seqlens_k:
         for hh in head_list:
             g = _backward_one(_as_f64(q[q0:q1, hh, :]), _as_f64(k[k0:k1, hh, :]),
                               _as_f64(v[k0:k1, hh, :]), _as_f64(dout[q0:q1, hh, :]),
-                              q1 - q0, causal, tau, row_block, rounding_scale)
+                              q1 - q0, causal, tau, row_block, rounding_scale,
+                              min(first_row, q1 - q0))
             for n, x in enumerate(g):
                 rows = slice(q0, q1) if n % 3 == 0 else slice(k0, k1)
                 outs[n][rows, hh, :] = x

@@ -34,12 +34,14 @@ Two answers are computed:
     inputs define; the P quantisation is the method's approximation, bounded
     by ``FP4Emulation.bound``.
   * ``attention_fp4pv_emulated``: the method's quantised result, computed from
-    the definition above in fp64, plus what is left ambiguous when the scores
-    are fp32 (as on the GPU): elements whose scaled value lies within a
-    relative 1e-4 of an e2m1 rounding midpoint may round either way, and a
-    group whose E_G argument lies within 1e-4 of an integer may take the
-    neighbouring exponent. Either choice is a correct result of the method; the
-    ``ambiguity`` term bounds how far the alternatives move O.
+    the definition above in fp64 (c = tau log2 e and every E_G and rounding
+    decided exactly), plus what is left ambiguous when the scores are fp32 (as
+    on the GPU): an element whose scaled value lies closer to an e2m1 rounding
+    midpoint, or a group whose E_G argument lies closer to an integer, than
+    the fp32 evaluation can be trusted (``oracle.fp32_window``) may take the
+    other branch. Either choice is a correct result of the method; the
+    ``ambiguity`` term is how far the other choices move O, and it is zero for
+    every element whose row has no such decision.
 """
 
 from __future__ import annotations
@@ -48,12 +50,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from . import fp32_window
 from .reference import _as_f64, attention, attention_sampled, visible
 
 E2M1_MAX = 6.0
 MX_BLOCK = 32                 # tokens per V scale block and per P group
 LOG2_6 = float(np.log2(6.0))
-AMBIGUOUS_REL = 1e-4          # see the module docstring
 
 
 def _e2m1_value(c: int) -> float:
@@ -149,27 +151,27 @@ def attention_fp4pv_sampled(q, k, v_packed, v_scales, cu_seqlens_q, cu_seqlens_k
     return attention_sampled(q, k, vh, cu_seqlens_q, cu_seqlens_k, causal, softmax_scale, samples)
 
 
-def fp32_log2e_scale(softmax_scale: float) -> float:
-    """c = fp32(fp32(softmax_scale) * log2 e): the exp2-domain score scale."""
-    return float(np.float32(np.float64(np.float32(softmax_scale)) / np.log(2.0)))
+def log2e_scale(softmax_scale: float) -> float:
+    """c = tau * log2 e in fp64, tau = fp32(softmax_scale) (what the kernel receives)."""
+    return float(np.float32(softmax_scale)) / float(np.log(2.0))
 
 
 def group_exponents(raw_gmax: np.ndarray, c: float):
-    """E_G = ceil(c g - log2 6) from fp32 group maxima, decided in fp32.
+    """E_G = ceil(c g - log2 6) from the exact group maxima, in fp64.
 
-    Returns (E as float64 with -inf for empty groups, frac = arg - floor(arg)
-    of the argument, NaN for empty groups). The argument is formed from the
-    fp32 score maximum with one rounding to fp32, as a fused multiply-add
-    computes it.
+    Returns (E as float64 with -inf for empty groups, the argument a = c g - log2 6).
     """
-    g32 = raw_gmax.astype(np.float32).astype(np.float64)
     with np.errstate(invalid="ignore"):
-        arg = (g32 * np.float64(np.float32(c)) - np.float64(np.float32(LOG2_6))).astype(np.float32)
-    arg = arg.astype(np.float64)
-    e = np.ceil(arg)
-    with np.errstate(invalid="ignore"):
-        frac = np.where(np.isfinite(arg), arg - np.floor(arg), np.nan)
-    return e, frac
+        arg = c * np.asarray(raw_gmax, dtype=np.float64) - LOG2_6
+    return np.ceil(arg), arg
+
+
+def _group_starts(key_tokens: np.ndarray):
+    blk = np.asarray(key_tokens) // MX_BLOCK
+    if not blk.size:
+        return np.zeros(0, dtype=np.intp), np.zeros(0, dtype=np.intp)
+    starts = np.flatnonzero(np.r_[True, blk[1:] != blk[:-1]])
+    return starts, np.diff(np.r_[starts, blk.size])
 
 
 def quantize_p_row_block(raw: np.ndarray, key_tokens: np.ndarray, c: float):
@@ -178,20 +180,18 @@ def quantize_p_row_block(raw: np.ndarray, key_tokens: np.ndarray, c: float):
     raw [r, sk] fp64 raw scores q.k of one (document, head); key_tokens [sk]
     the packed token index of each key (groups are the 32-token blocks).
     Returns (x [r, sk] = 2^(c r - E_G) before rounding, codes, E [r, sk]
-    (each key's group exponent), and the fractional part arg - floor(arg) of
-    each key's group exponent argument).
+    (each key's group exponent), and each key's group argument c g - log2 6).
     """
-    blk = np.asarray(key_tokens) // MX_BLOCK
-    starts = np.flatnonzero(np.r_[True, blk[1:] != blk[:-1]]) if blk.size else np.zeros(0, int)
-    counts = np.diff(np.r_[starts, blk.size])
-    gmax = np.maximum.reduceat(raw, starts, axis=1) if blk.size else np.zeros((raw.shape[0], 0))
-    e_g, frac_g = group_exponents(gmax, c)
+    starts, counts = _group_starts(key_tokens)
+    gmax = (np.maximum.reduceat(raw, starts, axis=1) if starts.size
+            else np.zeros((raw.shape[0], 0)))
+    e_g, arg_g = group_exponents(gmax, c)
     e = np.repeat(e_g, counts, axis=1)
-    frac = np.repeat(frac_g, counts, axis=1)
+    arg = np.repeat(arg_g, counts, axis=1)
     finite = np.isfinite(raw)
     with np.errstate(invalid="ignore", over="ignore"):
         x = np.where(finite, np.exp2(np.where(finite, c * raw - e, -np.inf)), 0.0)
-    return x, e2m1_encode(x), e, frac
+    return x, e2m1_encode(x), e, arg
 
 
 @dataclass
@@ -199,17 +199,36 @@ class FP4Emulation:
     out: np.ndarray        # [n, dv] emulated O
     lse: np.ndarray        # [n] LSE of the unquantised scores
     bound: np.ndarray      # [n, dv] bound on |O_emulated - O_exact|
-    ambiguity: np.ndarray  # [n, dv] how far the ambiguous roundings can move O
-    group_tie: np.ndarray  # [n] bool: some group exponent is a near tie (counted in ambiguity)
+    ambiguity: np.ndarray  # [n, dv] how far the fp32-ambiguous decisions can move O, in total
+    group_tie: np.ndarray  # [n] bool: some group exponent is ambiguous
+    key_tie: np.ndarray    # [n] int: keys whose e2m1 rounding is ambiguous
+    # per row, the signed change of O that each ambiguous decision's other
+    # branch makes ([K, dv], K = number of decisions), and what is left
+    # unlisted (second-order: a rounding that is ambiguous only on the other
+    # grid of an ambiguous group), as an elementwise allowance [dv]
+    alternatives: list = None
+    slack: np.ndarray = None
 
 
-def _fp4_rows(raw: np.ndarray, key_tokens: np.ndarray, vh: np.ndarray, c: float):
-    """Emulated O, LSE, error bound and ambiguity for rows of raw scores."""
+def _e2m1_neighbours(x: np.ndarray):
+    """The e2m1 values just below and just above x (0 <= x <= 6)."""
+    vals = e2m1_decode(_POS_CODES)
+    hi_idx = np.clip(np.searchsorted(vals, x, side="left"), 1, 7)
+    return vals[hi_idx - 1], vals[hi_idx]
+
+
+def _fp4_rows(raw: np.ndarray, absdot: np.ndarray, key_tokens: np.ndarray, vh: np.ndarray,
+              c: float, d: int):
+    """Emulated O, LSE, error bound and ambiguity for rows of raw scores.
+
+    absdot [r, sk] holds sum_t |q_t k_t| of each score (its fp32 error scale).
+    """
     r, dv = raw.shape[0], vh.shape[1]
     if raw.shape[1] == 0:      # a document without keys: O = 0, LSE = -inf
         z = np.zeros((r, dv))
-        return z, np.full(r, -np.inf), z.copy(), z.copy(), np.zeros(r, dtype=bool)
-    x, codes, e, frac = quantize_p_row_block(raw, key_tokens, c)
+        return (z, np.full(r, -np.inf), z.copy(), z.copy(), np.zeros(r, dtype=bool),
+                np.zeros(r, dtype=np.int64), [np.zeros((0, dv))] * r, z.copy())
+    x, codes, e, arg = quantize_p_row_block(raw, key_tokens, c)
     finite = np.isfinite(raw)
     any_vis = finite.any(axis=1)
     with np.errstate(invalid="ignore"):
@@ -225,26 +244,83 @@ def _fp4_rows(raw: np.ndarray, key_tokens: np.ndarray, vh: np.ndarray, c: float)
     # above 2 it is at most x/4
     err = rel * np.maximum(0.25, x / 4.0)
     bound = (err @ np.abs(vh)) * inv_l[:, None]
-    amb = np.where(_e2m1_midpoint_distance(x) < AMBIGUOUS_REL, rel * _e2m1_step(x), 0.0)
-    # a group whose exponent argument sits next to an integer may take the
-    # neighbouring exponent (E - 1 just above the integer, E + 1 just below):
-    # its keys' P_hat then follow the other grid
-    with np.errstate(invalid="ignore"):
-        below = finite & (frac < AMBIGUOUS_REL)            # ceil may have been one lower
-        above = finite & (frac > 1.0 - AMBIGUOUS_REL)      # ceil may have been one higher
-    tie = below | above
+
+    # decision 1: a scaled value next to an e2m1 rounding midpoint; the other
+    # branch takes the other neighbour of x on the grid
+    raw0 = np.where(finite, raw, 0.0)
+    x_err = fp32_window.rel_error_of_exp2(
+        fp32_window.arg_error(c, raw0, absdot, d, np.where(finite, c * raw0 - e, 0.0)))
+    key_amb = finite & fp32_window.within(_e2m1_midpoint_distance(x), x_err)
+    lo, hi = _e2m1_neighbours(np.minimum(x, E2M1_MAX))
+    chosen = e2m1_decode(codes)
+    key_delta = np.where(key_amb, (np.where(chosen == hi, lo, hi) - chosen) * rel, 0.0)
+    # decision 2: a group argument next to an integer. fp32 takes its maximum
+    # over fp32 scores, so the argument is off by the largest score error in
+    # the group; ceil may then land one lower or one higher, and the group's
+    # keys follow that other grid
+    starts, counts = _group_starts(key_tokens)
+    sc_err = np.where(finite, fp32_window.score_error(absdot, d), 0.0)
+    g_err = np.maximum.reduceat(sc_err, starts, axis=1)
+    gmax = np.maximum.reduceat(raw, starts, axis=1)
+    g_fin = np.isfinite(gmax)
+    _, g_arg = group_exponents(np.where(g_fin, gmax, 0.0), c)
+    a_err = np.where(g_fin, c * g_err + fp32_window.U32 * (c * np.abs(np.where(g_fin, gmax, 0.0))
+                                                           + np.abs(g_arg) + 3.0), 0.0)
+    win = fp32_window.SAFETY * a_err
+    e_lo, e_hi = np.ceil(g_arg - win), np.ceil(g_arg + win)
+    e_g = np.ceil(g_arg)
+    g_alt = np.where(e_lo != e_g, e_lo, np.where(e_hi != e_g, e_hi, np.nan))
+    g_tie = g_fin & np.isfinite(g_alt)
+    tie = np.repeat(g_tie, counts, axis=1) & finite
+    grp_delta = np.zeros_like(p_hat)
+    alt_slack = np.zeros_like(p_hat)
     if tie.any():
-        e_alt = np.where(below, e - 1.0, e + 1.0)
+        e_alt = np.repeat(np.where(g_tie, g_alt, 0.0), counts, axis=1)
         with np.errstate(invalid="ignore", over="ignore"):
             x_alt = np.where(tie, np.exp2(np.where(tie, c * raw - e_alt, -np.inf)), 0.0)
             rel_alt = np.where(tie, np.exp2(np.where(tie, e_alt, 0.0) - m[:, None]), 0.0)
         p_alt = e2m1_decode(e2m1_encode(x_alt)) * rel_alt
-        amb = amb + np.where(tie, np.abs(p_alt - p_hat), 0.0)
-    ambiguity = (amb @ np.abs(vh)) * inv_l[:, None]
+        grp_delta = np.where(tie, p_alt - p_hat, 0.0)
+        alt_amb = tie & fp32_window.within(_e2m1_midpoint_distance(x_alt), x_err)
+        alt_slack = np.where(alt_amb, rel_alt * _e2m1_step(x_alt), 0.0)
+    ambiguity = ((np.abs(key_delta) + np.abs(grp_delta) + alt_slack) @ np.abs(vh)) * inv_l[:, None]
+    slack = (alt_slack @ np.abs(vh)) * inv_l[:, None]
+    # the signed effect of each decision on O, per row (ties are sparse)
+    alternatives = []
+    key_group = np.repeat(np.arange(starts.size), counts)
+    for i in range(r):
+        rows = []
+        for j in np.flatnonzero(key_amb[i]):
+            rows.append(key_delta[i, j] * vh[j] * inv_l[i])
+        for gi in np.flatnonzero(g_tie[i]):
+            members = np.flatnonzero(key_group == gi)
+            rows.append((grp_delta[i, members] @ vh[members]) * inv_l[i])
+        alternatives.append(np.array(rows).reshape(len(rows), dv))
     group_tie = tie.any(axis=1)
     with np.errstate(divide="ignore"):
         lse = np.where(any_vis, (m + np.log2(np.where(any_vis, l, 1.0))) * np.log(2.0), -np.inf)
-    return out, lse, bound, ambiguity, group_tie
+    return (out, lse, bound, ambiguity, group_tie, key_amb.sum(axis=1), alternatives, slack)
+
+
+def outcome_within(o: np.ndarray, out: np.ndarray, alternatives: np.ndarray, slack: np.ndarray,
+                   bar: np.ndarray, max_enumerated: int = 10) -> bool:
+    """Whether O of one row lies within ``bar`` (+ slack) of some outcome of the method.
+
+    The outcomes are out + sum_k b_k alternatives[k] over b in {0, 1}^K: each
+    ambiguous decision taken either way. With more than ``max_enumerated``
+    decisions the largest are enumerated and the rest are added to the
+    allowance by their magnitude.
+    """
+    alts = np.asarray(alternatives).reshape(-1, out.shape[-1])
+    allow = bar + slack
+    if alts.shape[0] > max_enumerated:
+        order = np.argsort(-np.abs(alts).max(axis=1))
+        allow = allow + np.abs(alts[order[max_enumerated:]]).sum(axis=0)
+        alts = alts[order[:max_enumerated]]
+    k = alts.shape[0]
+    choices = ((np.arange(2 ** k)[:, None] >> np.arange(k)[None, :]) & 1).astype(np.float64)
+    cands = out[None, :] + choices @ alts
+    return bool((np.abs(o[None, :] - cands) <= allow[None, :]).all(axis=1).any())
 
 
 def attention_fp4pv_emulated(q, k, v_packed, v_scales, cu_seqlens_q, cu_seqlens_k,
@@ -262,10 +338,11 @@ def attention_fp4pv_emulated(q, k, v_packed, v_scales, cu_seqlens_q, cu_seqlens_
     samples = list(samples)
     vh_all = mx_dequantize_v(v_packed, v_scales, dq)
     dv = vh_all.shape[2]
-    c = fp32_log2e_scale(softmax_scale)
+    c = log2e_scale(softmax_scale)
     n = len(samples)
     res = FP4Emulation(np.zeros((n, dv)), np.zeros(n), np.zeros((n, dv)), np.zeros((n, dv)),
-                       np.zeros(n, dtype=bool))
+                       np.zeros(n, dtype=bool), np.zeros(n, dtype=np.int64), [None] * n,
+                       np.zeros((n, dv)))
     groups = {}
     for i, (t, hh) in enumerate(samples):
         b = int(np.searchsorted(cq, t, side="right") - 1)
@@ -280,12 +357,17 @@ def attention_fp4pv_emulated(q, k, v_packed, v_scales, cu_seqlens_q, cu_seqlens_
             idx = np.array([t for _, t in part])
             qb = _as_f64(q[idx.tolist(), hh, :])
             raw = qb @ kb.T
+            absdot = np.abs(qb) @ np.abs(kb).T
             vis = visible(idx - q0, q1 - q0, k1 - k0, causal)
             raw = np.where(vis, raw, -np.inf)
-            o, lse, bound, amb, tie = _fp4_rows(raw, key_tokens, vb, c)
+            o, lse, bound, amb, tie, nk, alts, slack = _fp4_rows(raw, absdot, key_tokens, vb, c,
+                                                                 dq)
             rows = np.array([i for i, _ in part])
             res.out[rows], res.lse[rows], res.bound[rows] = o, lse, bound
-            res.ambiguity[rows], res.group_tie[rows] = amb, tie
+            res.ambiguity[rows], res.group_tie[rows], res.key_tie[rows] = amb, tie, nk
+            res.slack[rows] = slack
+            for i_row, a in zip(rows, alts):
+                res.alternatives[i_row] = a
     return res
 
 
@@ -301,7 +383,7 @@ def attention_fp4pv_bruteforce(q, k, v_packed, v_scales, cu_seqlens_q, cu_seqlen
     import math
     qf, kf = _as_f64(q), _as_f64(k)
     vh = mx_dequantize_v(v_packed, v_scales, qf.shape[2])
-    c = fp32_log2e_scale(softmax_scale)
+    c = log2e_scale(softmax_scale)
     grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
     total_q, h, d = qf.shape
     dv = vh.shape[2]
@@ -328,9 +410,7 @@ def attention_fp4pv_bruteforce(q, k, v_packed, v_scales, cu_seqlens_q, cu_seqlen
                 for blk in sorted({(k0 + j) // MX_BLOCK for j in vis}):
                     members = [j for j in vis if (k0 + j) // MX_BLOCK == blk]
                     g = max(raw[j] for j in members)
-                    arg = float(np.float32(np.float64(np.float32(g)) * np.float64(np.float32(c))
-                                           - np.float64(np.float32(LOG2_6))))
-                    eg = math.ceil(arg)
+                    eg = math.ceil(c * g - math.log2(6.0))
                     for j in members:
                         weights[j] = nearest(2.0 ** (c * raw[j] - eg)) * 2.0 ** (eg - top)
                 lsum = math.fsum(2.0 ** (c * raw[j] - top) for j in vis)

@@ -5,11 +5,29 @@ TEST INFRASTRUCTURE (see ``oracle/reference.py``): imported only by tests,
 
 The fp8 P.V variant ("Kernel Bottleneck Tuning (validated on FA4 FP4/FP8 PV,
 GB300)", introduction and section 5) runs the second GEMM with P and V in
-e4m3. V reaches the kernel as e4m3 codes plus one fp32 scale per head. The
-oracle's answer for that workload is the exact attention of the inputs the
-kernel receives: Q and K in bf16 and V_hat = decode(codes) * scale[h], all in
-fp64. Rounding P to e4m3 is the kernel's approximation and is judged by the
-looser fp8 tolerance.
+e4m3. V reaches the kernel as e4m3 codes plus one fp32 scale per head. Two
+answers are computed:
+
+  * ``attention_fp8pv``: the exact attention of the inputs the kernel
+    receives, Q and K in bf16 and V_hat = decode(codes) * scale[h], in fp64;
+    rounding P to e4m3 is the method's approximation, judged by the looser
+    fp8 tolerance;
+  * ``attention_fp8pv_emulated``: the method's quantised result. With
+    c = tau log2 e and z_j = 2^(c s_j) the unnormalised exp2 weight of key j,
+    the method rounds P in the log domain ("Kernel Bottleneck Tuning", section
+    4: the scale is an addend of the exp2 argument) as
+        P_hat_j = 2^(M - 5) e4m3(2^(c s_j - M + 5))
+    with M an integer. Scaling by a power of two commutes with rounding to
+    e4m3 while the value stays in its normal range, so P_hat_j = R(z_j), the
+    rounding of z_j to e4m3 precision (4 significant bits, to nearest, ties to
+    even), whatever M is; the row sum keeps the unquantised z, so
+        O = scale[h] sum_j R(z_j) codes_j / sum_j z_j,  LSE = ln sum_j exp(tau s_j).
+    Keys more than 2^11 below the row's largest weight can fall in e4m3's
+    subnormal range, where the rounding depends on M: the oracle takes M at
+    its largest possible value and allows, per such key, what a smaller M can
+    change (``slack``). Where fp32 scores may round a weight the other way (it
+    sits next to an e4m3 midpoint closer than ``oracle.fp32_window`` trusts
+    fp32), the other rounding's effect on O is summed into ``ambiguity``.
 
 E4M3 (OCP 8-bit floating point, "FN" variant): 1 sign bit, 4 exponent bits with
 bias 7, 3 mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6; the
@@ -21,9 +39,15 @@ from __future__ import annotations
 
 import numpy as np
 
-from .reference import attention, attention_sampled
+from dataclasses import dataclass
+
+from . import fp32_window
+from .reference import _as_f64, attention, attention_sampled, visible
 
 E4M3_MAX = 448.0
+P_SCALE_LOG2 = 5              # the method's P scale, 2^5, an addend of the exp2 argument
+E4M3_MIN_NORMAL_LOG2 = -6     # smallest normal e4m3 value 2^-6
+E4M3_SUBNORMAL_STEP_LOG2 = -9  # spacing of the subnormal e4m3 values
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -96,46 +120,193 @@ def attention_fp8pv_sampled(q, k, v_codes, v_scale, cu_seqlens_q, cu_seqlens_k, 
                              causal, softmax_scale, samples)
 
 
-def attention_fp8pv_emulated(q, k, v_codes, v_scale, cu_seqlens_q, cu_seqlens_k, causal: bool,
-                             softmax_scale: float, p_scale_log2: float = 8.0):
-    """Diagnostic CPU emulation of the P quantisation (not a parity reference).
+def round_e4m3(x) -> np.ndarray:
+    """Round non-negative float64 values to the nearest e4m3 value, ties to even.
 
-    Per row, with m the row maximum of the scaled scores in base-2 units,
-    P_hat = e4m3(2^(s*log2e - m + p_scale_log2)); O = scale[h] * sum P_hat V_codes /
-    (2^p_scale_log2 * sum 2^(s*log2e - m)). The power-of-two P scale sits inside
-    the exponent, as the log-domain refactoring of "Kernel Bottleneck Tuning",
-    section 4, does with multiplicative scales. The GPU kernel quantises against
-    a running maximum instead of the final one, so the two agree only within the
-    fp8 tolerance, not bitwise.
+    Written from the format: a normal value keeps 4 significant bits, so
+    x = f 2^e with f in [0.5, 1) rounds to rint(16 f) 2^(e - 4) (numpy's rint
+    rounds halves to even, which is the even mantissa code); below 2^-6 the
+    values are multiples of 2^-9. Magnitudes above 448 saturate. The
+    exhaustive ``e4m3_encode`` pins it (tests/test_oracle_fp8.py).
     """
-    from .reference import _as_f64, visible
+    x = np.asarray(x, dtype=np.float64)
+    f, e = np.frexp(x)
+    normal = np.ldexp(np.rint(16.0 * f), e - 4)
+    sub = np.ldexp(np.rint(np.ldexp(x, 9)), -9)
+    return np.minimum(np.where(x < 2.0 ** E4M3_MIN_NORMAL_LOG2, sub, normal), E4M3_MAX)
+
+
+def _e4m3_midpoint_distance(x: np.ndarray) -> np.ndarray:
+    """Relative distance of x (> 0, e4m3 range) to the nearest e4m3 rounding midpoint."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    step = np.where(x < 2.0 ** E4M3_MIN_NORMAL_LOG2, 2.0 ** E4M3_SUBNORMAL_STEP_LOG2,
+                    np.ldexp(1.0, e - 4))
+    t = x / step
+    d = np.abs(t - (np.floor(t) + 0.5)) * step
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(x > 0, d / x, np.inf)
+
+
+def _e4m3_step(x: np.ndarray) -> np.ndarray:
+    """Spacing of the e4m3 values around x (the cost of a flipped rounding)."""
+    _, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.where(x < 2.0 ** E4M3_MIN_NORMAL_LOG2, 2.0 ** E4M3_SUBNORMAL_STEP_LOG2,
+                    np.ldexp(1.0, e - 4))
+
+
+@dataclass
+class FP8Emulation:
+    out: np.ndarray        # [n, dv] emulated O
+    lse: np.ndarray        # [n] LSE of the unquantised scores
+    bound: np.ndarray      # [n, dv] |O_emulated - O_exact| bound (sum |R(z) - z| |V| / l)
+    ambiguity: np.ndarray  # [n, dv] how far fp32-ambiguous roundings can move O, in total
+    slack: np.ndarray      # [n, dv] what the subnormal band's dependence on M can change
+    key_tie: np.ndarray    # [n] int: keys whose rounding is ambiguous
+
+
+def log2e_scale(softmax_scale: float) -> float:
+    """c = tau * log2 e in fp64, tau = fp32(softmax_scale) (what the kernel receives)."""
+    return float(np.float32(softmax_scale)) / float(np.log(2.0))
+
+
+def _fp8_rows(raw: np.ndarray, absdot: np.ndarray, vq: np.ndarray, c: float, d: int):
+    """Emulated O (before the per-head V scale), LSE, bound, ambiguity, slack."""
+    r, dv = raw.shape[0], vq.shape[1]
+    finite = np.isfinite(raw)
+    any_vis = finite.any(axis=1)
+    raw0 = np.where(finite, raw, 0.0)
+    with np.errstate(invalid="ignore"):
+        top = np.where(any_vis, np.max(np.where(finite, c * raw, -np.inf), axis=1), 0.0)
+    # the largest integer maximum fp32 can reach: ceil of c * (row maximum) plus
+    # its fp32 error window
+    top_err = np.where(any_vis, np.max(np.where(
+        finite, fp32_window.arg_error(c, raw0, absdot, d, c * raw0), 0.0), axis=1), 0.0)
+    m_hi = np.ceil(top + fp32_window.SAFETY * top_err)
+    # x = 2^(c s - M + 5) at M = m_hi, everything else relative to 2^m_hi
+    with np.errstate(invalid="ignore", over="ignore"):
+        arg = np.where(finite, c * raw0 - m_hi[:, None] + P_SCALE_LOG2, -np.inf)
+        x = np.where(finite, np.exp2(arg), 0.0)
+    xq = round_e4m3(x)
+    scale_row = 2.0 ** -P_SCALE_LOG2           # z / 2^m_hi = x 2^-5
+    z = x * scale_row
+    ref = xq * scale_row
+    l = z.sum(axis=1)
+    inv_l = np.where(any_vis, 1.0 / np.where(any_vis, l, 1.0), 0.0)
+    out = (ref @ vq) * inv_l[:, None]
+    bound = (np.abs(ref - z) @ np.abs(vq)) * inv_l[:, None]
+    # keys that are normal at every possible M <= m_hi: x >= 2^-6 at M = m_hi
+    tail = finite & (x < 2.0 ** E4M3_MIN_NORMAL_LOG2)
+    # a tail key rounds within min(z, half a subnormal step at m_hi) + 2^-4 z of z
+    # whatever M is, and so does the reference: twice that between the two
+    half_sub = 2.0 ** (E4M3_SUBNORMAL_STEP_LOG2 - 1) * scale_row
+    tail_gap = np.where(tail, 2.0 * (np.minimum(z, half_sub) + z / 16.0), 0.0)
+    slack = (tail_gap @ np.abs(vq)) * inv_l[:, None]
+    # normal-range keys next to a rounding midpoint
+    x_err = fp32_window.rel_error_of_exp2(
+        fp32_window.arg_error(c, raw0, absdot, d, np.where(finite, arg, 0.0)))
+    amb_key = finite & ~tail & fp32_window.within(_e4m3_midpoint_distance(x), x_err)
+    amb = np.where(amb_key, _e4m3_step(x) * scale_row, 0.0)
+    ambiguity = (amb @ np.abs(vq)) * inv_l[:, None]
+    with np.errstate(divide="ignore"):
+        lse = np.where(any_vis, (m_hi + np.log2(np.where(any_vis, l, 1.0))) * np.log(2.0),
+                       -np.inf)
+    return out, lse, bound, ambiguity, slack, amb_key.sum(axis=1)
+
+
+def attention_fp8pv_emulated(q, k, v_codes, v_scale, cu_seqlens_q, cu_seqlens_k, causal: bool,
+                             softmax_scale: float, samples=None) -> FP8Emulation:
+    """The method's fp8 P.V result for (token, head) samples (all if None).
+
+    ``samples`` is an iterable of (global query token, head); results follow
+    its order, each row computed from its complete score row.
+    """
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    total_q, h, dq = q.shape
+    if samples is None:
+        samples = [(t, hh) for t in range(total_q) for hh in range(h)]
+    samples = list(samples)
+    codes = v_codes.numpy() if hasattr(v_codes, "numpy") else np.asarray(v_codes)
+    vq_all = e4m3_decode(codes)
+    vs = (v_scale.double().numpy() if hasattr(v_scale, "double")
+          else np.asarray(v_scale, np.float64))
+    dv = vq_all.shape[2]
+    c = log2e_scale(softmax_scale)
+    n = len(samples)
+    res = FP8Emulation(np.zeros((n, dv)), np.zeros(n), np.zeros((n, dv)), np.zeros((n, dv)),
+                       np.zeros((n, dv)), np.zeros(n, dtype=np.int64))
+    groups = {}
+    for i, (t, hh) in enumerate(samples):
+        b = int(np.searchsorted(cq, t, side="right") - 1)
+        groups.setdefault((b, int(hh)), []).append((i, int(t)))
+    for (b, hh), items in groups.items():
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        kb = _as_f64(k[k0:k1, hh, :])
+        vb = vq_all[k0:k1, hh, :]
+        for s0 in range(0, len(items), 256):
+            part = items[s0:s0 + 256]
+            idx = np.array([t for _, t in part])
+            rows = np.array([i for i, _ in part])
+            if k1 == k0:       # a document without keys: O = 0, LSE = -inf
+                res.lse[rows] = -np.inf
+                continue
+            qb = _as_f64(q[idx.tolist(), hh, :])
+            raw = qb @ kb.T
+            absdot = np.abs(qb) @ np.abs(kb).T
+            vis = visible(idx - q0, q1 - q0, k1 - k0, causal)
+            raw = np.where(vis, raw, -np.inf)
+            o, lse, bound, amb, slack, nk = _fp8_rows(raw, absdot, vb, c, dq)
+            sv = vs[hh]
+            res.out[rows], res.lse[rows], res.bound[rows] = sv * o, lse, sv * bound
+            res.ambiguity[rows], res.slack[rows], res.key_tie[rows] = sv * amb, sv * slack, nk
+    return res
+
+
+def attention_fp8pv_bruteforce(q, k, v_codes, v_scale, cu_seqlens_q, cu_seqlens_k,
+                               causal: bool, softmax_scale: float):
+    """Pure-Python loops over rows and keys; tiny inputs only.
+
+    The method's weights written element by element from the definition: each
+    z_j = 2^(c s_j) rounded to the nearest value with 4 significant bits (the
+    candidates (8 + i) 2^(e - 3), i = 0..8, around 2^e <= z_j < 2^(e+1);
+    ties to an even i), O = scale[h] sum R(z_j) V_j / sum z_j. For inputs whose
+    weights all lie within 2^11 of the row's largest (no subnormal band).
+    Returns O [total_q, h, dv].
+    """
+    import math
     qf, kf = _as_f64(q), _as_f64(k)
     codes = v_codes.numpy() if hasattr(v_codes, "numpy") else np.asarray(v_codes)
     vq = e4m3_decode(codes)
-    scale = v_scale.double().numpy() if hasattr(v_scale, "double") else np.asarray(v_scale, np.float64)
-    tau = float(np.float32(softmax_scale))
-    total_q, h, _ = qf.shape
+    vs = (v_scale.double().numpy() if hasattr(v_scale, "double")
+          else np.asarray(v_scale, np.float64))
+    c = float(np.float32(softmax_scale)) / math.log(2.0)
+    total_q, h, d = qf.shape
     dv = vq.shape[2]
     out = np.zeros((total_q, h, dv))
-    lse = np.full((h, total_q), -np.inf)
-    log2e = 1.0 / np.log(2.0)
+
+    def r4(zv):
+        e = math.floor(math.log2(zv))
+        cands = [(8 + i) * 2.0 ** (e - 3) for i in range(9)]
+        return cands[min(range(9), key=lambda i: (abs(cands[i] - zv), i % 2))]
+
     for b in range(len(cu_seqlens_q) - 1):
         q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
         k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
         sq, sk = q1 - q0, k1 - k0
         for hh in range(h):
-            s2 = tau * log2e * (qf[q0:q1, hh] @ kf[k0:k1, hh].T)
-            vis = visible(np.arange(sq), sq, sk, causal)
-            s2 = np.where(vis, s2, -np.inf)
-            m = s2.max(axis=1) if sk else np.full(sq, -np.inf)
-            ok = np.isfinite(m)
-            m0 = np.where(ok, m, 0.0)
-            e = np.exp2(s2 - m0[:, None])
-            l = e.sum(axis=1)
-            ph = e4m3_decode(e4m3_encode(np.minimum(e * 2.0 ** p_scale_log2, E4M3_MAX)))
-            num = ph @ vq[k0:k1, hh]
-            den = np.where(ok, l * 2.0 ** p_scale_log2, 1.0)
-            out[q0:q1, hh] = np.where(ok[:, None], scale[hh] * num / den[:, None], 0.0)
-            with np.errstate(divide="ignore"):
-                lse[hh, q0:q1] = np.where(ok, (m0 + np.log2(np.where(ok, l, 1.0))) * np.log(2.0), -np.inf)
-    return out, lse
+            for i in range(sq):
+                vis = [j for j in range(sk) if (not causal) or j <= i + sk - sq]
+                if not vis:
+                    continue
+                s = {j: math.fsum(float(qf[q0 + i, hh, t]) * float(kf[k0 + j, hh, t])
+                                  for t in range(d)) for j in vis}
+                top = max(c * s[j] for j in vis)
+                # weights relative to 2^top (a power-of-two shift leaves R unchanged)
+                shift = math.floor(top)
+                z = {j: 2.0 ** (c * s[j] - shift) for j in vis}
+                lsum = math.fsum(z.values())
+                for t in range(dv):
+                    out[q0 + i, hh, t] = vs[hh] * math.fsum(r4(z[j]) * vq[k0 + j, hh, t]
+                                                            for j in vis) / lsum
+    return out

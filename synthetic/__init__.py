@@ -137,7 +137,9 @@ WORKLOADS = {
 # Extra shapes for measurement only (not among the five above): the c4 token
 # layout without the causal mask, which isolates the cost of causal scheduling;
 # a short query range against long keys (few query blocks: the shape split-KV
-# is for); and the c5 shape with P.V in fp4 (MXFP4 V, per-group e2m1 P).
+# is for); the c5 shape with P.V in fp4 (MXFP4 V, per-group e2m1 P); and the
+# c5 shape in bf16, the third of the fwd+bwd shapes the FA4 spill issue times
+# (one 32768-token document, 16 heads).
 EXTRA_WORKLOADS = {
     "x_varlen_noncausal_32k": Workload(
         "x_varlen_noncausal_32k", "varlen non-causal: 32768 tokens / 8 docs, h=32 d=128",
@@ -148,6 +150,9 @@ EXTRA_WORKLOADS = {
     "x_causal_fp4pv_32k": Workload(
         "x_causal_fp4pv_32k", "single-doc causal fp4 P.V: 32768 tokens, h=16 d=128",
         heads=16, head_dim=128, causal=True, doc_lens=_linspace_docs(32768, 1), fp4_pv=True),
+    "x_causal_bf16_32k": Workload(
+        "x_causal_bf16_32k", "single-doc causal bf16: 32768 tokens, h=16 d=128",
+        heads=16, head_dim=128, causal=True, doc_lens=_linspace_docs(32768, 1)),
 }
 
 

@@ -183,6 +183,37 @@ def test_bwd_varlen_causal_full_size_sampled(name):
     assert all(np.isfinite(g).all() for g in got)
 
 
+def test_bwd_single_document_32k_sampled():
+    """The third shape the FA4 spill issue times fwd+bwd: one 32768-token causal
+    document, 16 heads, d = 128, at full size with dO = 2 O / n on the checked
+    head (from the library's own forward O, which is the step's input), an
+    N(0, 1) draw times 2 / n elsewhere. Checked on one head: dQ of the last 2048
+    query rows, and dK, dV of the last 2048 keys (those rows alone see them),
+    every gradient for finiteness."""
+    import head_attention_forward_fmha_amd as fm
+    from synthetic import EXTRA_WORKLOADS
+    w = EXTRA_WORKLOADS["x_causal_bf16_32k"]
+    inp = workload_inputs(w)
+    dev = _dev()
+    cq = torch.from_numpy(np.asarray(inp.cu_q, np.int32)).to(dev)
+    o_dev, _ = fm.fwd(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), cq, cq, w.max_seqlen_q,
+                      w.max_seqlen_k, causal=True, softmax_scale=w.softmax_scale)
+    n = w.total_q * w.heads * w.head_dim
+    head = 5
+    dout = make_dout(w.total_q, w.heads, w.head_dim, seed=w.seed).float() * (2.0 / n)
+    dout[:, head] = o_dev[:, head].float().cpu() * (2.0 / n)
+    dout = dout.to(torch.bfloat16)
+    got = _gpu_bwd(inp, dout, True, w.softmax_scale)
+    first = w.total_q - 2048
+    ref, t = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, True,
+                                       w.softmax_scale, heads=[head], rounding_scale=True,
+                                       first_row=first)
+    tail = slice(first, w.total_q)
+    _check([g[tail][:, [head]] for g in got], [r[tail][:, [head]] for r in ref],
+           [x[tail][:, [head]] for x in t], f"{w.name} head {head}, last 2048 rows and keys")
+    assert all(np.isfinite(g).all() for g in got)
+
+
 def test_bwd_dense_layout_matches_packed():
     import head_attention_forward_fmha_amd as fm
     dev = _dev()

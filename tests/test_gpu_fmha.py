@@ -3,10 +3,17 @@
 Bar (bf16): |O_gpu - O_ref| <= 1e-2 + 1e-2 |O_ref| elementwise and
 |LSE_gpu - LSE_ref| <= 1e-3 on finite rows, -inf rows matching exactly.
 Bar (fp8 P.V): |O_gpu - O_ref| <= 5e-2 + 5e-2 |O_ref|, LSE as for bf16 (the row
-sum is taken before P is rounded to e4m3).
+sum is taken before P is rounded to e4m3). That bar alone passes an all-zero O
+on long rows (|O| is about 0.01 there), so fp8 outputs are also held to the
+method's own quantised result (``oracle.attention_fp8pv_emulated``) at the
+bf16 bar, widened only by the oracle's fp32-ambiguity and subnormal-band
+allowances.
+
+Every check also reports the error normalised by the row RMS of O_ref and
+holds it to a derived bar (tests/parity.py), which stays sharp on long rows.
 
 The five workloads are checked at their full sizes in the launch configuration
-the benchmark times: the small ones on every output, the large ones on sampled
+the benchmark times: c1, c2 and c3 on every output, c4 and c5 on sampled
 (token, head) rows the oracle computes one by one (each from its complete score
 row). Edge cases cover ragged tails, empty documents, sq != sk with causal
 bottom-right alignment, d = 64, and tiny documents.
@@ -20,6 +27,7 @@ import torch
 
 import oracle
 from synthetic import WORKLOADS, make_inputs, workload_inputs
+from tests.parity import NORMALISED_BAR, error_summary, fp8_emulation_check
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +67,10 @@ def _run(inp, causal, scale, heads, d, fp8=False, max_q=None, max_k=None, varian
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def _check(o, lse, o_ref, lse_ref, fp8=False, what=""):
+def _check(o, lse, o_ref, lse_ref, fp8=False, what="", emu=None):
+    """The stated bar against the exact oracle; the normalised error against the
+    exact oracle (bf16) or against the emulated method ``emu`` (fp8, rows in
+    o's row order after reshaping to [rows, d])."""
     atol, rtol = (O_ATOL_FP8, O_RTOL_FP8) if fp8 else (O_ATOL, O_RTOL)
     assert not np.isnan(o).any(), f"{what}: NaN in O (unwritten or invalid output)"
     err = np.abs(o - o_ref)
@@ -68,6 +79,29 @@ def _check(o, lse, o_ref, lse_ref, fp8=False, what=""):
         idx = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(o_ref))), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} O elements out of tolerance; worst at {idx}: "
                              f"gpu {o[idx]} ref {o_ref[idx]} (max abs err {err.max():.3e})")
+    d = o.shape[-1]
+    if not fp8:
+        summ = error_summary(o.reshape(-1, d), o_ref.reshape(-1, d), atol, rtol)
+    else:
+        assert emu is not None, "fp8 outputs are also checked against the emulated method"
+        o2 = o.reshape(-1, d)
+        ok = fp8_emulation_check(o2, emu)
+        assert ok.all(), (f"{what}: {int((~ok).sum())} rows off the emulated fp8 method; first "
+                          f"row {int(np.argmin(ok))}")
+        # normalised error with the fp32 allowances taken off first
+        allow = emu.ambiguity + emu.slack
+        summ = error_summary(o2, emu.out, 1e-2, 1e-2, extra=allow)
+        resid = np.maximum(np.abs(o2 - emu.out) - allow, 0.0)
+        rms = np.sqrt((emu.out ** 2).mean(axis=1))
+        live = rms > 0
+        summ["max_normalised_err"] = float((resid[live].max(axis=1) / rms[live]).max()) \
+            if live.any() else 0.0
+    print(f"{what}: max abs err {summ['max_abs_err']:.3e}, max normalised err "
+          f"{summ['max_normalised_err']:.3e}, rms err {summ['rms_err']:.3e}, over bar "
+          f"{summ['n_over_bar']}, worst at {summ['worst_location']}")
+    assert summ["max_normalised_err"] <= NORMALISED_BAR, (
+        f"{what}: normalised O error {summ['max_normalised_err']:.3e} > {NORMALISED_BAR} "
+        f"(row {summ['worst_normalised_row']})")
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isneginf(lse), ~fin), f"{what}: -inf LSE rows differ"
     if fin.any():
@@ -80,12 +114,15 @@ def _full_parity(lens, heads, d, causal, seed=0, scale=None, fp8=False, max_q=No
     inp = make_inputs(lens, heads, d, seed=seed, fp8_pv=fp8)
     scale = float(np.float32(1.0 / np.sqrt(d))) if scale is None else scale
     o, lse = _run(inp, causal, scale, heads, d, fp8=fp8, max_q=max_q, max_k=max_k, variant=variant)
+    emu = None
     if fp8:
         o_ref, lse_ref = oracle.attention_fp8pv(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
                                                 inp.cu_k, causal, scale)
+        emu = oracle.attention_fp8pv_emulated(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                              inp.cu_k, causal, scale)
     else:
         o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
-    _check(o, lse, o_ref, lse_ref, fp8=fp8,
+    _check(o, lse, o_ref, lse_ref, fp8=fp8, emu=emu,
            what=f"lens={lens} h={heads} d={d} causal={causal} variant={variant}")
     return inp, o, lse
 
@@ -110,16 +147,20 @@ def _sampled_parity(w, n_random=1500, seed=0, variant="auto"):
     o, lse = _run(inp, w.causal, w.softmax_scale, w.heads, w.head_dim, fp8=w.fp8_pv,
                   variant=variant)
     samples = _sample_rows(inp.cu_q, w.heads, n_random, seed)
+    emu = None
     if w.fp8_pv:
         o_ref, l_ref = oracle.attention_fp8pv_sampled(inp.q, inp.k, inp.v_e4m3, inp.v_scale,
                                                       inp.cu_q, inp.cu_k, w.causal,
                                                       w.softmax_scale, samples)
+        emu = oracle.attention_fp8pv_emulated(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                              inp.cu_k, w.causal, w.softmax_scale,
+                                              samples=samples)
     else:
         o_ref, l_ref = oracle.attention_sampled(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, w.causal,
                                                 w.softmax_scale, samples)
     t = np.array([a for a, _ in samples])
     hh = np.array([b for _, b in samples])
-    _check(o[t, hh], lse[hh, t], o_ref, l_ref, fp8=w.fp8_pv, what=w.name)
+    _check(o[t, hh], lse[hh, t], o_ref, l_ref, fp8=w.fp8_pv, what=w.name, emu=emu)
     # every output element was written and finite
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     return o, lse
@@ -156,8 +197,26 @@ def test_c2_dense_layout_matches_packed():
 
 
 @pytest.mark.parametrize("variant", ["auto", "pipelined"])
-def test_c3_varlen_causal_8k_sampled(variant):
-    _sampled_parity(WORKLOADS["c3_varlen_causal_8k"], variant=variant)
+def test_c3_varlen_causal_8k_full(variant):
+    """c3 at full size, every (token, head, d) output against the full oracle."""
+    w = WORKLOADS["c3_varlen_causal_8k"]
+    inp = workload_inputs(w)
+    o, lse = _run(inp, w.causal, w.softmax_scale, w.heads, w.head_dim, variant=variant)
+    o_ref, lse_ref = _c3_oracle()
+    _check(o, lse, o_ref, lse_ref, what=f"{w.name} {variant}")
+
+
+_C3_CACHE = {}
+
+
+def _c3_oracle():
+    """The full c3 oracle (a few seconds on the host's cores), computed once."""
+    if "c3" not in _C3_CACHE:
+        w = WORKLOADS["c3_varlen_causal_8k"]
+        inp = workload_inputs(w)
+        _C3_CACHE["c3"] = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, w.causal,
+                                           w.softmax_scale)
+    return _C3_CACHE["c3"]
 
 
 @pytest.mark.parametrize("variant", ["auto", "pipelined"])
@@ -171,6 +230,8 @@ def test_c2_dense_2225_pipelined():
 
 
 def test_c5_causal_fp8pv_32k_sampled():
+    """c5 at full size on sampled rows: the stated fp8 bar against the exact
+    attention of the dequantised V, and the emulated method at the bf16 bar."""
     _sampled_parity(WORKLOADS["c5_causal_fp8pv_32k"], n_random=600)
 
 
@@ -359,7 +420,10 @@ def test_rows_after_the_last_document_are_never_read(fp8, variant, causal):
                               77, causal=causal, softmax_scale=scale, variant=variant)
         o_ref, l_ref = oracle.attention_fp8pv(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
                                               inp.cu_k, causal, scale)
+        emu = oracle.attention_fp8pv_emulated(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                              inp.cu_k, causal, scale)
     else:
+        emu = None
         v_buf = torch.full((total_k + pad, heads, d), float("nan"), dtype=torch.bfloat16,
                            device=dev)
         v_buf[:total_k] = inp.v.to(dev)
@@ -368,4 +432,4 @@ def test_rows_after_the_last_document_are_never_read(fp8, variant, causal):
         o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
     torch.cuda.synchronize()
     _check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
-           o_ref, l_ref, fp8=fp8, what=f"NaN-padded K/V, fp8={fp8}, {variant}")
+           o_ref, l_ref, fp8=fp8, what=f"NaN-padded K/V, fp8={fp8}, {variant}", emu=emu)

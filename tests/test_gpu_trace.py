@@ -2,7 +2,9 @@
 
 The traced launch runs the same ping-pong kernel arithmetic as the forward
 pass, so its outputs must equal the untraced kernel's bit for bit, for every
-P.V format and both trace modes. The records must follow the kernel's schedule:
+P.V format and both trace modes, and meet the oracle's bars as the forward
+pass does ("Kernel Bottleneck Tuning", section 6: every build, instrumented or
+not, is checked against the reference). The records must follow the kernel's schedule:
 a work item of n key tiles runs slot pairs j = 0 .. n, so a wave records one
 item start, 2n + 3 slot starts (one before each slot and one after the last
 barrier, which opens the epilogue) and, per slot, one phase-end mark (coarse)
@@ -25,15 +27,43 @@ def _dev():
     return torch.device("cuda:0")
 
 
-def _inputs(lens, heads, pv, seed):
+def _inputs(lens, heads, pv, seed, with_host=False):
     inp = make_inputs(lens, heads, 128, seed=seed, fp8_pv=pv == "e4m3", fp4_pv=pv == "e2m1")
     dev = _dev()
     v = {"bf16": inp.v, "e4m3": inp.v_e4m3, "e2m1": inp.v_e2m1}[pv].to(dev)
     vs = {"bf16": None, "e4m3": inp.v_scale, "e2m1": inp.v_mx_scale}[pv]
     cu = torch.from_numpy(np.asarray(inp.cu_q, np.int32)).to(dev)
     ck = torch.from_numpy(np.asarray(inp.cu_k, np.int32)).to(dev)
-    return (inp.q.to(dev), inp.k.to(dev), v, None if vs is None else vs.to(dev), cu, ck,
+    args = (inp.q.to(dev), inp.k.to(dev), v, None if vs is None else vs.to(dev), cu, ck,
             int(np.diff(inp.cu_q).max()), int(np.diff(inp.cu_k).max()))
+    return (args, inp) if with_host else args
+
+
+def _check_against_oracle(pv, inp, o, lse, what):
+    """The forward pass's parity checks, applied to a traced launch's outputs."""
+    import oracle
+    from tests import test_gpu_fmha as gf
+    from tests import test_gpu_fp4 as g4
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    if pv == "bf16":
+        o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, True, scale)
+        gf._check(o, lse, o_ref, l_ref, what=what)
+    elif pv == "e4m3":
+        o_ref, l_ref = oracle.attention_fp8pv(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                              inp.cu_k, True, scale)
+        emu = oracle.attention_fp8pv_emulated(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                              inp.cu_k, True, scale)
+        gf._check(o, lse, o_ref, l_ref, fp8=True, emu=emu, what=what)
+    else:
+        tq, h = inp.q.shape[0], inp.q.shape[1]
+        emu = oracle.attention_fp4pv_emulated(inp.q, inp.k, inp.v_e2m1, inp.v_mx_scale, inp.cu_q,
+                                              inp.cu_k, True, scale)
+        o_x, l_x = oracle.attention_fp4pv(inp.q, inp.k, inp.v_e2m1, inp.v_mx_scale, inp.cu_q,
+                                          inp.cu_k, True, scale)
+        g4._check(o.reshape(tq * h, -1), lse.T.reshape(-1), emu, o_x.reshape(tq * h, -1),
+                  l_x.T.reshape(-1), what=what)
 
 
 def _untraced(pv, q, k, v, vs, cu, ck, mq, mk):
@@ -49,12 +79,14 @@ def _untraced(pv, q, k, v, vs, cu, ck, mq, mk):
 @pytest.mark.parametrize("detailed", [False, True])
 def test_traced_outputs_equal_the_untraced_kernel(pv, detailed):
     import head_attention_forward_fmha_amd as fm
-    args = _inputs(((700, 700), (333, 333), (1, 1), (1300, 1300)), 4, pv, seed=3)
+    args, inp = _inputs(((700, 700), (333, 333), (1, 1), (1300, 1300)), 4, pv, seed=3,
+                        with_host=True)
     o0, l0 = _untraced(pv, *args)
     q, k, v, vs, cu, ck, mq, mk = args
     o1, l1, trace = fm.fwd_trace(q, k, v, cu, ck, mq, mk, pv=pv, v_scale=vs, detailed=detailed,
                                  traced_workgroups=8)
     torch.cuda.synchronize()
+    _check_against_oracle(pv, inp, o1, l1, what=f"traced {pv} detailed={detailed}")
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
     s = pt.summarize(trace.cpu().numpy().view(np.uint64))
     assert s["waves"] > 0 and s["period"] > 0

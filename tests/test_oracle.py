@@ -281,7 +281,25 @@ def _mut_scale_squared(q, k, tau):
     return tau * tau * (q @ k.T)
 
 
+def _mut_scale_dropped(q, k, tau):
+    return q @ k.T
+
+
+def _mut_scores_transposed(q, k, tau):
+    # the score matrix taken in the wrong orientation: S^T where it is square,
+    # the keys in reverse order otherwise
+    s = tau * (q @ k.T)
+    return s.T if s.shape[0] == s.shape[1] else s[:, ::-1]
+
+
+def _mut_values_transposed(q, k, v, rows, sq, causal, tau):
+    # O = P V with V's rows taken in reverse key order (an index mistake on the
+    # second operand)
+    return _orig_attention_rows(q, k, v[::-1], rows, sq, causal, tau)
+
+
 _orig_softmax = oa.softmax_rows
+_orig_attention_rows = oa.attention_rows
 
 
 @pytest.mark.parametrize("target,mutant", [
@@ -290,6 +308,9 @@ _orig_softmax = oa.softmax_rows
     ("softmax_rows", _mut_lse_drops_max),
     ("softmax_rows", _mut_no_max_subtraction_sign),
     ("scores", _mut_scale_squared),
+    ("scores", _mut_scale_dropped),
+    ("scores", _mut_scores_transposed),
+    ("attention_rows", _mut_values_transposed),
 ])
 def test_mutants_are_caught(monkeypatch, target, mutant):
     assert _pins_pass()

@@ -19,6 +19,7 @@ import pytest
 import torch
 
 import oracle
+from synthetic import make_dout, make_inputs
 
 LENS = ((5, 5), (3, 7), (6, 2), (0, 3), (4, 0), (1, 1))
 
@@ -186,3 +187,70 @@ def test_rounding_scale_covers_bf16_operands(causal):
     # the scale is a small fraction of the gradients' size, not a blanket allowance
     for r, t in zip(ref, scale):
         assert np.median(t) < 5e-3 * np.sqrt(np.mean(r * r))
+
+
+def test_skipping_first_rows_leaves_the_rest_exact():
+    """first_row only drops work: every gradient it still reports equals the full
+    computation's (up to the summation order of its row blocks), and the ones it
+    cannot know are NaN."""
+    inp = make_inputs(((70, 70), (50, 60)), 2, 16, seed=8)
+    dout = make_dout(inp.q.shape[0], 2, 16, seed=8)
+    for causal in (False, True):
+        full = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, causal,
+                                         0.25, row_block=16)
+        part = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, causal,
+                                         0.25, row_block=16, first_row=33)
+        for f, g in zip(full, part):
+            known = ~np.isnan(g)
+            assert np.allclose(f[known], g[known], rtol=1e-12, atol=1e-15)
+        dq, dk, _ = part
+        assert np.isnan(dq[:33]).all() and not np.isnan(dq[33:70]).any()
+        if causal:    # doc 0: keys 33..69 are seen only by rows >= 33
+            assert np.isnan(dk[:33]).all() and not np.isnan(dk[33:70]).any()
+            # doc 1 (sq 50, sk 60): rows >= 33 alone see keys >= 43
+            assert np.isnan(dk[70:70 + 43]).all() and not np.isnan(dk[70 + 43:]).any()
+        else:
+            assert np.isnan(dk).all()
+
+
+# ---------------------------------------------------------------------------
+# Mutation check: planted mistakes in a copy of the oracle's per-head
+# backward must each fail a pin above.
+# ---------------------------------------------------------------------------
+
+def _pins_pass():
+    try:
+        for causal in (False, True):
+            test_finite_differences(causal)
+            test_invariants(causal)
+            test_torch_autograd_dense(causal)
+    except AssertionError:
+        return False
+    return True
+
+
+_MUTATIONS = {
+    # dS = P * dP: the softmax Jacobian's row term dropped
+    "dropped_jacobian_term": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))",
+                              "ds = p * dp"),
+    # dK = tau dS^T Q with dS^T's rows taken in the wrong (reversed) key order
+    "transposed_dk": ("dk += tau * (ds.T @ qb[r0:r1])", "dk += tau * (ds.T[::-1] @ qb[r0:r1])"),
+    # dV from P without the transpose, reading keys in reverse order
+    "dv_wrong_orientation": ("dv += p.T @ dob[r0:r1]", "dv += p.T[::-1] @ dob[r0:r1]"),
+    # dQ without the softmax scale
+    "dq_scale_dropped": ("dq[r0:r1] = tau * (ds @ kb)", "dq[r0:r1] = ds @ kb"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_MUTATIONS))
+def test_backward_mutants_are_caught(monkeypatch, name):
+    import inspect
+    from oracle import backward as ob
+    assert _pins_pass()
+    old, new = _MUTATIONS[name]
+    src = inspect.getsource(ob._backward_one)
+    assert old in src, f"mutation site for {name} not found"
+    ns = dict(vars(ob))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(ob, "_backward_one", ns["_backward_one"])
+    assert not _pins_pass(), f"planted mistake {name} was not caught"
