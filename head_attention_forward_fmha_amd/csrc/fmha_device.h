@@ -53,10 +53,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 64;     // keys per K/V tile
 constexpr int kXcds = 8;    // accelerator complex dies of an MI355X
-// fp8 P.V: P is quantised as e4m3(2^(c s - M + 5)) with M an integer running
-// maximum in exp2 units, so a key at the row maximum scales to at most 2^5 and
-// the lazy raise below has a factor 14 of headroom under e4m3's maximum 448;
-// values down to 2^-11 of the maximum stay in e4m3's normal range.
+// fp8 P.V: P is quantised as e4m3(2^(c s - A + 5)) with A a running anchor in
+// exp2 units (softmax_e4m3), so a key at the anchor scales to 2^5 and the lazy
+// raise has a factor 14 of headroom under e4m3's maximum 448; values down to
+// 2^-11 of the anchor stay in e4m3's normal range.
 constexpr float kPScaleLog2 = 5.f;
 constexpr float kE4m3Max = 448.f;
 
@@ -348,7 +348,7 @@ struct WaveTile {
   static constexpr int kKeyBlocks = kBN / 32;            // S^T accumulator blocks
   static constexpr int kVReads = kFp8 ? 1 : 2;
   // bf16 P tolerates p up to 2^8 (lazy maximum); e4m3 P up to its largest
-  // finite value (kE4m3Max), with the integer maximum of softmax_e4m3.
+  // finite value (kE4m3Max), with the stepped anchor of softmax_e4m3.
   static constexpr float kLazyLimit = 256.f;  // 2^8: largest p the bf16 path allows
   static_assert(kLoadsPerWave >= 1 && kLoadsPerWave * kThreads * 16 == kTileBytes,
                 "K tile must split into whole lane loads");
@@ -370,7 +370,7 @@ struct WaveTile {
   i32x4 pb4;             // e2m1 P of the last softmaxed tile (32 keys per lane)
   int p_scale;           // its E8M0 group scale for this lane's 32 keys
   float m_run, l_run, c;
-  float m_log2;          // e4m3 and e2m1 paths: integer running maximum in exp2 units
+  float m_log2;          // e4m3: running anchor; e2m1: integer running maximum (exp2 units)
   int key_lo;            // keys before this are hidden (block-aligned fp4 tiles)
   // per-lane LDS byte offsets of the operand reads within a stage's tile
   int k_off[kKSteps];
@@ -750,17 +750,19 @@ struct WaveTile {
     l_run += lane_sum;
   }
 
-  // e4m3 P: an integer running maximum M in exp2 units, raised lazily. The
-  // tile's values x = exp2(fma(s, c, 5 - M)) are rounded to e4m3 and summed
-  // in fp32; M is kept as long as no x exceeds e4m3's largest value, checked
-  // on each lane's partial sum (every x is at most that sum). A row that
-  // exceeds it, or has no maximum yet, takes M = ceil(c * tile row max), so its
-  // x are at most 2^5, and the wave redoes the tile. Every O and l rescale is
-  // then an exact power of two, 2^(M_old - M_new), and because scaling by a
-  // power of two commutes with rounding to e4m3 in its normal range, the
-  // quantised P times 2^(M - 5) is the e4m3-precision rounding of 2^(c s)
-  // whatever M is: P_hat depends on the scores alone (below 2^-6 of the
-  // scale, in e4m3's subnormal range, on M as well).
+  // e4m3 P: a running anchor A in exp2 units, raised lazily by whole steps.
+  // The tile's values x = exp2(fma(s, c, 5 - A)) are rounded to e4m3 and summed
+  // in fp32; A is kept as long as no x exceeds e4m3's largest value, checked
+  // on each lane's partial sum (every x is at most that sum). A row's first
+  // maximum sets A = c * (its first tile's row maximum), so that key maps to
+  // exactly 2^5; afterwards a row that exceeds the limit raises A by the whole
+  // number of steps that brings its tile's maximum under 2^5, and the wave
+  // redoes the tile. Every later O and l rescale is then an exact power of
+  // two, and because scaling by a power of two commutes with rounding to e4m3
+  // in its normal range, the quantised P times 2^(A - 5) is the e4m3-precision
+  // rounding of 2^(c s) on the grid that the first anchor fixes, whatever the
+  // later steps are: P_hat depends on the scores alone (below 2^-6 of the
+  // scale, in e4m3's subnormal range, on the steps as well).
   __device__ __forceinline__ void softmax_e4m3() {
     float rs[4];
     exp_sum_convert(rs);
@@ -771,14 +773,15 @@ struct WaveTile {
     if (mask != 0) {
       const uint32_t rows = (uint32_t)mask | (uint32_t)(mask >> 32);
       const bool row_raise = (rows >> col) & 1u;
-      // -inf for a row that sees no key yet, which keeps M = -inf
-      const float cand = __builtin_ceilf(tile_row_max() * c);
-      const bool up = row_raise && (cand > m_log2);
-      const float m_new = up ? cand : m_log2;
-      // 2^(M_old - M_new): 1 for rows not raised, 0 for a first maximum (the
-      // clamp also absorbs -inf and the NaN of -inf - -inf, where O = l = 0)
-      const float alpha = __builtin_ldexpf(1.f, (int)fmaxf(m_log2 - m_new, -200.f));
-      m_log2 = m_new;
+      const float cmx = tile_row_max() * c;   // -inf for a row that sees no key yet
+      const bool first = m_log2 == -__builtin_inff();
+      // whole steps for a raised anchor (NaN when both are -inf, never used)
+      const float steps = __builtin_ceilf(cmx - m_log2);
+      const bool up = row_raise && (first ? cmx > -__builtin_inff() : steps > 0.f);
+      // 2^(A_old - A_new): 1 for rows not raised, 0 for a first maximum (O = l = 0)
+      float alpha = 1.f;
+      if (up) alpha = first ? 0.f : __builtin_ldexpf(1.f, -(int)steps);
+      m_log2 = up ? (first ? cmx : m_log2 + steps) : m_log2;
       rescale(alpha);
       exp_sum_convert(rs);
       lane_sum = (rs[0] + rs[1]) + (rs[2] + rs[3]);
@@ -808,8 +811,8 @@ struct WaveTile {
   // p = exp2(fma(s, c, -c*m_run)) for the 32 scores of this lane (the scale and
   // the row maximum folded into one multiply-add), partial row sums of the fp32
   // p in four chains, and P rounded for the P.V operand: bf16 RNE, or e4m3 of
-  // exp2(fma(s, c, kPScaleLog2 - M)), the scale and the integer maximum folded
-  // into the addend. The scores in sacc are kept.
+  // exp2(fma(s, c, kPScaleLog2 - A)), the scale and the anchor folded into the
+  // addend. The scores in sacc are kept.
   __device__ __forceinline__ void exp_sum_convert(float (&rs)[4]) {
     // an all-masked row keeps the fold finite
     float p_add;

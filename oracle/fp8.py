@@ -16,18 +16,22 @@ answers are computed:
     c = tau log2 e and z_j = 2^(c s_j) the unnormalised exp2 weight of key j,
     the method rounds P in the log domain ("Kernel Bottleneck Tuning", section
     4: the scale is an addend of the exp2 argument) as
-        P_hat_j = 2^(M - 5) e4m3(2^(c s_j - M + 5))
-    with M an integer. Scaling by a power of two commutes with rounding to
-    e4m3 while the value stays in its normal range, so P_hat_j = R(z_j), the
-    rounding of z_j to e4m3 precision (4 significant bits, to nearest, ties to
-    even), whatever M is; the row sum keeps the unquantised z, so
-        O = scale[h] sum_j R(z_j) codes_j / sum_j z_j,  LSE = ln sum_j exp(tau s_j).
-    Keys more than 2^11 below the row's largest weight can fall in e4m3's
-    subnormal range, where the rounding depends on M: the oracle takes M at
-    its largest possible value and allows, per such key, what a smaller M can
-    change (``slack``). Where fp32 scores may round a weight the other way (it
-    sits next to an e4m3 midpoint closer than ``oracle.fp32_window`` trusts
-    fp32), the other rounding's effect on O is summed into ``ambiguity``.
+        P_hat_j = 2^(A - 5) e4m3(2^(c s_j - A + 5))
+    with the anchor A = a + K: a = c m0, m0 the row's largest score among the
+    document's first 64 keys (the first tile, where the row's first maximum
+    is taken), and K a whole number of steps. Scaling by a power of two
+    commutes with rounding to e4m3 while the value stays in its normal range,
+    so P_hat_j = 2^a R(z_j / 2^a), with R the rounding to e4m3 precision (4
+    significant bits, to nearest, ties to even), whatever K is; the first
+    tile's largest key maps exactly. The row sum keeps the unquantised z, so
+        O = scale[h] sum_j P_hat_j codes_j / sum_j z_j,  LSE = ln sum_j exp(tau s_j).
+    Keys more than 2^11 below the anchor can fall in e4m3's subnormal range,
+    where the rounding depends on K: the oracle takes K at its largest
+    possible value and allows, per such key, what a smaller K can change
+    (``slack``). Where fp32 scores may round a weight the other way (it sits
+    next to an e4m3 midpoint closer than ``oracle.fp32_window`` trusts fp32,
+    anchor included), the other rounding's effect on O is summed into
+    ``ambiguity``.
 
 E4M3 (OCP 8-bit floating point, "FN" variant): 1 sign bit, 4 exponent bits with
 bias 7, 3 mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6; the
@@ -48,6 +52,7 @@ E4M3_MAX = 448.0
 P_SCALE_LOG2 = 5              # the method's P scale, 2^5, an addend of the exp2 argument
 E4M3_MIN_NORMAL_LOG2 = -6     # smallest normal e4m3 value 2^-6
 E4M3_SUBNORMAL_STEP_LOG2 = -9  # spacing of the subnormal e4m3 values
+FIRST_TILE_KEYS = 64           # keys of the tile where a row's first maximum is taken
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -171,45 +176,62 @@ def log2e_scale(softmax_scale: float) -> float:
 
 
 def _fp8_rows(raw: np.ndarray, absdot: np.ndarray, vq: np.ndarray, c: float, d: int):
-    """Emulated O (before the per-head V scale), LSE, bound, ambiguity, slack."""
+    """Emulated O (before the per-head V scale), LSE, bound, ambiguity, slack.
+
+    raw [r, sk] holds the rows' raw scores over the document's keys in order
+    (masked keys -inf); absdot the sums of |q_t k_t| (fp32 error scales)."""
     r, dv = raw.shape[0], vq.shape[1]
     finite = np.isfinite(raw)
     any_vis = finite.any(axis=1)
     raw0 = np.where(finite, raw, 0.0)
     with np.errstate(invalid="ignore"):
         top = np.where(any_vis, np.max(np.where(finite, c * raw, -np.inf), axis=1), 0.0)
-    # the largest integer maximum fp32 can reach: ceil of c * (row maximum) plus
-    # its fp32 error window
+        first = raw[:, :FIRST_TILE_KEYS]
+        first_vis = np.isfinite(first).any(axis=1)
+        a = np.where(first_vis, c * np.max(np.where(np.isfinite(first), first, -np.inf), axis=1),
+                     top)
+    sc_err = fp32_window.score_error(absdot, d)
+    # fp32 forms the first anchor from the largest fp32 score of the first tile
+    a_err = np.where(any_vis, c * np.max(np.where(np.isfinite(first),
+                                                  sc_err[:, :FIRST_TILE_KEYS], 0.0), axis=1),
+                     0.0) + 3 * fp32_window.U32 * np.abs(a)
     top_err = np.where(any_vis, np.max(np.where(
         finite, fp32_window.arg_error(c, raw0, absdot, d, c * raw0), 0.0), axis=1), 0.0)
-    m_hi = np.ceil(top + fp32_window.SAFETY * top_err)
-    # x = 2^(c s - M + 5) at M = m_hi, everything else relative to 2^m_hi
+    # the highest anchor the row can reach: a plus the whole steps to the row's
+    # largest weight, with fp32's error taken in the direction of more steps
+    k_hi = np.maximum(np.ceil(top - a + fp32_window.SAFETY * (top_err + a_err)), 0.0)
+    a_hi = a + k_hi
+    # x = 2^(c s - A + 5) at A = a_hi; weights z relative to 2^a_hi
     with np.errstate(invalid="ignore", over="ignore"):
-        arg = np.where(finite, c * raw0 - m_hi[:, None] + P_SCALE_LOG2, -np.inf)
+        arg = np.where(finite, c * raw0 - a_hi[:, None] + P_SCALE_LOG2, -np.inf)
         x = np.where(finite, np.exp2(arg), 0.0)
     xq = round_e4m3(x)
-    scale_row = 2.0 ** -P_SCALE_LOG2           # z / 2^m_hi = x 2^-5
+    scale_row = 2.0 ** -P_SCALE_LOG2
     z = x * scale_row
     ref = xq * scale_row
     l = z.sum(axis=1)
     inv_l = np.where(any_vis, 1.0 / np.where(any_vis, l, 1.0), 0.0)
     out = (ref @ vq) * inv_l[:, None]
     bound = (np.abs(ref - z) @ np.abs(vq)) * inv_l[:, None]
-    # keys that are normal at every possible M <= m_hi: x >= 2^-6 at M = m_hi
+    # keys normal at every anchor the row can reach: x >= 2^-6 at the highest
     tail = finite & (x < 2.0 ** E4M3_MIN_NORMAL_LOG2)
-    # a tail key rounds within min(z, half a subnormal step at m_hi) + 2^-4 z of z
-    # whatever M is, and so does the reference: twice that between the two
+    # a tail key rounds within min(z, half a subnormal step at a_hi) + 2^-4 z of z
+    # whatever the steps are, and so does the reference: twice that between them
     half_sub = 2.0 ** (E4M3_SUBNORMAL_STEP_LOG2 - 1) * scale_row
     tail_gap = np.where(tail, 2.0 * (np.minimum(z, half_sub) + z / 16.0), 0.0)
     slack = (tail_gap @ np.abs(vq)) * inv_l[:, None]
-    # normal-range keys next to a rounding midpoint
+    # normal-range keys next to a rounding midpoint: the argument's fp32 error
+    # is its own plus the anchor's (first anchor, whole steps added in fp32,
+    # and the addend 5 - A)
+    anchor_err = a_err + fp32_window.U32 * (2 * np.abs(a_hi) + P_SCALE_LOG2)
     x_err = fp32_window.rel_error_of_exp2(
-        fp32_window.arg_error(c, raw0, absdot, d, np.where(finite, arg, 0.0)))
+        fp32_window.arg_error(c, raw0, absdot, d, np.where(finite, arg, 0.0))
+        + anchor_err[:, None])
     amb_key = finite & ~tail & fp32_window.within(_e4m3_midpoint_distance(x), x_err)
     amb = np.where(amb_key, _e4m3_step(x) * scale_row, 0.0)
     ambiguity = (amb @ np.abs(vq)) * inv_l[:, None]
     with np.errstate(divide="ignore"):
-        lse = np.where(any_vis, (m_hi + np.log2(np.where(any_vis, l, 1.0))) * np.log(2.0),
+        lse = np.where(any_vis, (a_hi + np.log2(np.where(any_vis, l, 1.0))) * np.log(2.0),
                        -np.inf)
     return out, lse, bound, ambiguity, slack, amb_key.sum(axis=1)
 
@@ -267,12 +289,13 @@ def attention_fp8pv_bruteforce(q, k, v_codes, v_scale, cu_seqlens_q, cu_seqlens_
                                causal: bool, softmax_scale: float):
     """Pure-Python loops over rows and keys; tiny inputs only.
 
-    The method's weights written element by element from the definition: each
-    z_j = 2^(c s_j) rounded to the nearest value with 4 significant bits (the
-    candidates (8 + i) 2^(e - 3), i = 0..8, around 2^e <= z_j < 2^(e+1);
-    ties to an even i), O = scale[h] sum R(z_j) V_j / sum z_j. For inputs whose
-    weights all lie within 2^11 of the row's largest (no subnormal band).
-    Returns O [total_q, h, dv].
+    The method's weights written element by element from the definition: with
+    a = c m0 (m0 the row's largest visible score among the document's first 64
+    keys), each w_j = 2^(c s_j - a) rounded to the nearest value with 4
+    significant bits (the candidates (8 + i) 2^(e - 3), i = 0..8, around
+    2^e <= w_j < 2^(e+1); ties to an even i), O = scale[h] sum R(w_j) V_j /
+    sum w_j. For inputs whose weights all lie within 2^11 of the anchor (no
+    subnormal band). Returns O [total_q, h, dv].
     """
     import math
     qf, kf = _as_f64(q), _as_f64(k)
@@ -285,10 +308,10 @@ def attention_fp8pv_bruteforce(q, k, v_codes, v_scale, cu_seqlens_q, cu_seqlens_
     dv = vq.shape[2]
     out = np.zeros((total_q, h, dv))
 
-    def r4(zv):
-        e = math.floor(math.log2(zv))
+    def r4(wv):
+        e = math.floor(math.log2(wv))
         cands = [(8 + i) * 2.0 ** (e - 3) for i in range(9)]
-        return cands[min(range(9), key=lambda i: (abs(cands[i] - zv), i % 2))]
+        return cands[min(range(9), key=lambda i: (abs(cands[i] - wv), i % 2))]
 
     for b in range(len(cu_seqlens_q) - 1):
         q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
@@ -301,12 +324,10 @@ def attention_fp8pv_bruteforce(q, k, v_codes, v_scale, cu_seqlens_q, cu_seqlens_
                     continue
                 s = {j: math.fsum(float(qf[q0 + i, hh, t]) * float(kf[k0 + j, hh, t])
                                   for t in range(d)) for j in vis}
-                top = max(c * s[j] for j in vis)
-                # weights relative to 2^top (a power-of-two shift leaves R unchanged)
-                shift = math.floor(top)
-                z = {j: 2.0 ** (c * s[j] - shift) for j in vis}
-                lsum = math.fsum(z.values())
+                a = c * max(s[j] for j in vis if j < FIRST_TILE_KEYS)
+                w = {j: 2.0 ** (c * s[j] - a) for j in vis}
+                lsum = math.fsum(w.values())
                 for t in range(dv):
-                    out[q0 + i, hh, t] = vs[hh] * math.fsum(r4(z[j]) * vq[k0 + j, hh, t]
+                    out[q0 + i, hh, t] = vs[hh] * math.fsum(r4(w[j]) * vq[k0 + j, hh, t]
                                                             for j in vis) / lsum
     return out

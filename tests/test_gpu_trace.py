@@ -55,7 +55,7 @@ def _check_against_oracle(pv, inp, o, lse, what):
                                               inp.cu_k, True, scale)
         emu = oracle.attention_fp8pv_emulated(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
                                               inp.cu_k, True, scale)
-        gf._check(o, lse, o_ref, l_ref, fp8=True, emu=emu, what=what, stated_fp8_bar=False)
+        gf._check(o, lse, o_ref, l_ref, fp8=True, emu=emu, what=what)
     else:
         tq, h = inp.q.shape[0], inp.q.shape[1]
         emu = oracle.attention_fp4pv_emulated(inp.q, inp.k, inp.v_e2m1, inp.v_mx_scale, inp.cu_q,
