@@ -19,9 +19,10 @@ import math
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import FMHA_OK, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
+from ._lib import FMHA_OK, NOALLOC_SCRATCH_BYTES, VARIANTS, FmhaError, EXPORTED_SYMBOLS  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "bwd", "bwd_workspace_size", "fwd_splitkv", "splitkv_num_splits",
+__all__ = ["fwd", "fwd_fp8pv", "fwd_fp4pv", "bwd", "bwd_noalloc", "bwd_workspace_size", "fwd_splitkv",
+           "splitkv_num_splits", "NOALLOC_SCRATCH_BYTES",
            "splitkv_workspace_size", "merge_partials", "fwd_trace", "TRACE_EVENTS_PER_WAVE",
            "auto_variant", "validate_cu_seqlens", "status_string", "abi_version",
            "FmhaError", "EXPORTED_SYMBOLS", "VARIANTS", "load_library"]
@@ -323,6 +324,47 @@ def bwd(q, k, v, out, dout, lse, cu_seqlens_q=None, cu_seqlens_k=None,
                       ws_bytes, ctypes.c_void_p(_stream_handle(dev)))
     if st != FMHA_OK:
         raise FmhaError(st, "fmha_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q=None, cu_seqlens_k=None,
+                max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                causal: bool = False, softmax_scale: Optional[float] = None) -> Tuple:
+    """``bwd`` without a workspace: the library's fixed per-GPU array of
+    NOALLOC_SCRATCH_BYTES holds D and LSE*log2(e), so neither this call nor the
+    library allocates (the caller passes dq, dk, dv). Calls that can overlap on
+    one GPU share that array and must be ordered by the caller. Problems with
+    heads * total_q above NOALLOC_SCRATCH_BYTES / 8 raise FmhaError."""
+    import torch
+    lib = _lib.load()
+    dev = q.device
+    for name, t, ref in (("q", q, q), ("k", k, q), ("v", v, q), ("out", out, q),
+                         ("dout", dout, q)):
+        _check_tensor(name, t, torch.bfloat16, ref.dim(), dev)
+    s = _prepare(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if k.shape != v.shape or k.shape[-2:] != q.shape[-2:]:
+        raise ValueError("k and v must match, with q's heads and head_dim")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    _check_tensor("lse", lse, torch.float32, 2, dev)
+    if tuple(lse.shape) != (s["heads"], s["lse_len"]):
+        raise ValueError("lse must be [heads, total_q]")
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, torch.bfloat16, ref.dim(), dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have the shape of its input")
+    if 8 * s["heads"] * s["total_q"] > NOALLOC_SCRATCH_BYTES:
+        raise FmhaError(2, f"fmha_bwd_noalloc: heads * total_q = {s['heads'] * s['total_q']} "
+                           f"exceeds the {NOALLOC_SCRATCH_BYTES >> 20} MiB scratch "
+                           f"({NOALLOC_SCRATCH_BYTES // 8} rows)")
+    scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)
+    st = lib.fmha_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                              _ptr(s["cu_q"]), _ptr(s["cu_k"]), s["batch"], s["total_q"],
+                              s["total_k"], s["max_q"], s["max_k"], s["heads"], s["d"],
+                              int(bool(causal)), ctypes.c_float(scale), _ptr(dq), _ptr(dk),
+                              _ptr(dv), ctypes.c_void_p(_stream_handle(dev)))
+    if st != FMHA_OK:
+        raise FmhaError(st, "fmha_bwd_noalloc")
     return dq, dk, dv
 
 

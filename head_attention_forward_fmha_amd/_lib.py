@@ -17,6 +17,7 @@ FMHA_OK = 0
 FMHA_ERR_INVALID_ARG = 1
 FMHA_ERR_UNSUPPORTED = 2
 FMHA_ERR_LAUNCH = 3
+NOALLOC_SCRATCH_BYTES = 16 << 20      # FMHA_NOALLOC_SCRATCH_BYTES of include/fmha.h
 
 VARIANTS = {"auto": 0, "four_wave": 1, "pingpong": 2, "pipelined": 3}
 
@@ -34,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "fmha_fwd_trace",
     "fmha_bwd",
     "fmha_bwd_workspace_size",
+    "fmha_bwd_noalloc",
     "fmha_fwd_auto_variant",
     "fmha_validate_cu_seqlens",
     "fmha_status_string",
@@ -108,6 +110,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmha_bwd.argtypes = ([_vp] * 8 + [_i32] * 8 + [_f32] + [_vp] * 4 +
                              [ctypes.c_size_t, _vp])
     lib.fmha_bwd.restype = ctypes.c_int
+    # fmha_bwd's arguments without workspace and workspace bytes
+    lib.fmha_bwd_noalloc.argtypes = [_vp] * 8 + [_i32] * 8 + [_f32] + [_vp] * 4
+    lib.fmha_bwd_noalloc.restype = ctypes.c_int
     lib.fmha_bwd_workspace_size.argtypes = [_i32, _i32]
     lib.fmha_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fmha_fwd_auto_variant.argtypes = [_i32, _i32, _i32]

@@ -2,11 +2,15 @@
 //
 // Host-side argument validation happens before any HIP call, so the checks
 // run (and are tested) on machines without a GPU. The library allocates
-// nothing and keeps no state; launches go to the caller's stream.
+// nothing; launches go to the caller's stream. Its one piece of state is the
+// fixed device array below that fmha_bwd_noalloc uses as its workspace, and
+// that array's address on each device.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "fmha.h"
 #include "fmha_bwd_params.h"
@@ -20,9 +24,38 @@ static_assert(FMHA_TRACE_EV_SLOT == fmha::kEvSlot && FMHA_TRACE_EV_QK_DONE == fm
                   FMHA_TRACE_EV_WAIT_DONE == fmha::kEvWaitDone && FMHA_TRACE_EV_ITEM == fmha::kEvItem,
               "trace event codes");
 
+// Workspace of fmha_bwd_noalloc: a file-scope device array, one copy per GPU,
+// held until the process ends. Host code never passes its name to a kernel (on
+// the host the name is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[FMHA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Device addresses of `scratch`, one per device, looked up on the first
+// fmha_bwd_noalloc call on that device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+hipError_t scratch_address(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -259,6 +292,67 @@ size_t fmha_bwd_workspace_size(int32_t total_q, int32_t num_heads) {
   return 2 * (size_t)total_q * (size_t)num_heads * sizeof(float);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks of the backward's arguments other than its workspace.
+fmha_status_t check_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, const int32_t* cu_q,
+                        const int32_t* cu_k, int32_t batch, int32_t total_q, int32_t total_k,
+                        int32_t max_q, int32_t max_k, int32_t heads, int32_t head_dim,
+                        int32_t causal, float scale, const void* dq, const void* dk,
+                        const void* dv) {
+  fmha_status_t st = check_common(q, k, v, cu_q, cu_k, batch, total_q, total_k, max_q, max_k,
+                                  heads, head_dim, causal, scale, out, lse);
+  if (st != FMHA_OK) return st;
+  if (total_q > 0 && (dout == nullptr || lse == nullptr || dq == nullptr))
+    return FMHA_ERR_INVALID_ARG;
+  if (total_k > 0 && (dk == nullptr || dv == nullptr)) return FMHA_ERR_INVALID_ARG;
+  if ((dout && !aligned16(dout)) || (dq && !aligned16(dq)) || (dk && !aligned16(dk)) ||
+      (dv && !aligned16(dv)))
+    return FMHA_ERR_INVALID_ARG;
+  if (((int64_t)max_k + 127) / 128 * heads * batch > INT32_MAX) return FMHA_ERR_UNSUPPORTED;
+  return FMHA_OK;
+}
+
+// The two backward launches, with the workspace at `workspace` (checked).
+fmha_status_t launch_backward(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, const int32_t* cu_q,
+                              const int32_t* cu_k, int32_t batch, int32_t total_q,
+                              int32_t total_k, int32_t max_q, int32_t max_k, int32_t heads,
+                              int32_t head_dim, int32_t causal, float scale, void* dq, void* dk,
+                              void* dv, void* workspace, hipStream_t stream) {
+  fmha::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.cu_q = cu_q;
+  p.cu_k = cu_k;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = static_cast<float*>(workspace);
+  p.lse2 = p.delta + (size_t)total_q * heads;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.max_seqlen_q = max_q;
+  p.max_seqlen_k = max_k;
+  p.heads = heads;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  const hipError_t e = fmha::launch_bwd(p, head_dim, causal != 0, stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
 fmha_status_t fmha_bwd(const void* q, const void* k, const void* v, const void* out,
                        const void* dout, const float* lse,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -268,46 +362,42 @@ fmha_status_t fmha_bwd(const void* q, const void* k, const void* v, const void* 
                        int32_t causal, float softmax_scale,
                        void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  fmha_status_t st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
-                                  max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
-                                  softmax_scale, out, lse);
+  fmha_status_t st = check_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, batch,
+                               total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim,
+                               causal, softmax_scale, dq, dk, dv);
   if (st != FMHA_OK) return st;
-  if (total_q > 0 && (dout == nullptr || lse == nullptr || dq == nullptr))
-    return FMHA_ERR_INVALID_ARG;
-  if (total_k > 0 && (dk == nullptr || dv == nullptr)) return FMHA_ERR_INVALID_ARG;
-  if ((dout && !aligned16(dout)) || (dq && !aligned16(dq)) || (dk && !aligned16(dk)) ||
-      (dv && !aligned16(dv)))
-    return FMHA_ERR_INVALID_ARG;
-  if (((int64_t)max_seqlen_k + 127) / 128 * num_heads * batch > INT32_MAX)
-    return FMHA_ERR_UNSUPPORTED;
   const size_t need = fmha_bwd_workspace_size(total_q, num_heads);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
     return FMHA_ERR_INVALID_ARG;
   if (batch == 0 || (total_q == 0 && total_k == 0)) return FMHA_OK;
-  fmha::BwdParams p{};
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.out = out;
-  p.dout = dout;
-  p.lse = lse;
-  p.cu_q = cu_seqlens_q;
-  p.cu_k = cu_seqlens_k;
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  p.delta = static_cast<float*>(workspace);
-  p.lse2 = p.delta + (size_t)total_q * num_heads;
-  p.batch = batch;
-  p.total_q = total_q;
-  p.total_k = total_k;
-  p.max_seqlen_q = max_seqlen_q;
-  p.max_seqlen_k = max_seqlen_k;
-  p.heads = num_heads;
-  p.scale = softmax_scale;
-  p.scale_log2 = softmax_scale * kLog2e;
-  const hipError_t e = fmha::launch_bwd(p, head_dim, causal != 0, (hipStream_t)stream);
-  return e == hipSuccess ? FMHA_OK : FMHA_ERR_LAUNCH;
+  return launch_backward(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                         total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
+                         softmax_scale, dq, dk, dv, workspace, (hipStream_t)stream);
+}
+
+fmha_status_t fmha_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads, int32_t head_dim,
+                               int32_t causal, float softmax_scale,
+                               void* dq, void* dk, void* dv, void* stream) {
+  fmha_status_t st = check_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, batch,
+                               total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim,
+                               causal, softmax_scale, dq, dk, dv);
+  if (st != FMHA_OK) return st;
+  if (fmha_bwd_workspace_size(total_q, num_heads) > (size_t)FMHA_NOALLOC_SCRATCH_BYTES)
+    return FMHA_ERR_UNSUPPORTED;
+  if (batch == 0 || (total_q == 0 && total_k == 0)) return FMHA_OK;
+  // D and LSE * log2(e) go to this device's copy of the fixed array. Every row
+  // they are read at is written first by the same call's dQ launch, so the
+  // previous call's contents need no clearing.
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return FMHA_ERR_LAUNCH;
+  return launch_backward(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q,
+                         total_k, max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
+                         softmax_scale, dq, dk, dv, ws, (hipStream_t)stream);
 }
 
 fmha_status_t fmha_merge_partials(const float* o_part, const float* lse_part, int32_t num_parts,

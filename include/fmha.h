@@ -338,6 +338,34 @@ fmha_status_t fmha_bwd(const void* q, const void* k, const void* v, const void* 
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fmha_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid allocation. Same arguments, results and errors
+ * as fmha_bwd (bitwise the same dQ, dK, dV). D and LSE * log2(e) go to a
+ * fixed device array of FMHA_NOALLOC_SCRATCH_BYTES inside the library, one
+ * copy per GPU, which each GPU holds until the process ends; its address is
+ * looked up (hipGetSymbolAddress, no allocation) on the first call on a device.
+ * The call allocates nothing.
+ *   limit     fmha_bwd_workspace_size(total_q, num_heads) <= FMHA_NOALLOC_SCRATCH_BYTES,
+ *             i.e. num_heads * total_q <= 2^21 (c4: 2^20); larger problems
+ *             return FMHA_ERR_UNSUPPORTED before any HIP call
+ *   sharing   every call on a GPU uses that GPU's one array: calls that can
+ *             overlap on one GPU (other streams, other threads) race and must
+ *             be ordered by the caller; sequential calls on one stream are safe
+ *   device    the current device must be the stream's device
+ * A failed address lookup returns FMHA_ERR_LAUNCH.
+ */
+#define FMHA_NOALLOC_SCRATCH_BYTES (16u << 20)
+fmha_status_t fmha_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads, int32_t head_dim,
+                               int32_t causal, float softmax_scale,
+                               void* dq, void* dk, void* dv, void* stream);
+
+/*
  * The kernel variant FMHA_VARIANT_AUTO resolves to for a problem of `batch`
  * documents, longest query document max_seqlen_q and num_heads heads:
  * FMHA_VARIANT_FOUR_WAVE or FMHA_VARIANT_PINGPONG. Negative sizes give -1.
@@ -359,7 +387,7 @@ const char* fmha_status_string(fmha_status_t status);
 /* ABI version of this header: (major << 16) | minor. */
 int32_t fmha_abi_version(void);
 
-#define FMHA_ABI_VERSION ((1 << 16) | 4)
+#define FMHA_ABI_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
                             "fmha_fwd_fp8pv_variant", "fmha_fwd_fp4pv", "fmha_fwd_fp4pv_variant",
                             "fmha_fwd_splitkv", "fmha_fwd_splitkv_workspace_size",
                             "fmha_fwd_splitkv_num_splits", "fmha_merge_partials", "fmha_fwd_trace",
-                            "fmha_bwd", "fmha_bwd_workspace_size", "fmha_fwd_auto_variant", "fmha_validate_cu_seqlens",
+                            "fmha_bwd", "fmha_bwd_workspace_size", "fmha_bwd_noalloc",
+                            "fmha_fwd_auto_variant", "fmha_validate_cu_seqlens",
                             "fmha_status_string", "fmha_abi_version"])
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert set(fm.EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert fm.abi_version() == (1 << 16) | 4
+    assert fm.abi_version() == (1 << 16) | 5
 
 
 def test_status_strings():
@@ -241,6 +242,44 @@ def test_bwd_argument_checks():
     # nothing to compute: no launch
     empty = [None] * 8 + [0, 0, 0, 0, 0, 2, 64, 0, ctypes.c_float(0.125)] + [None] * 4 + [0, None]
     assert lib.fmha_bwd(*empty) == 0
+
+
+def test_bwd_noalloc_argument_checks():
+    """fmha_bwd_noalloc checks fmha_bwd's arguments, then its scratch limit
+    (heads * total_q * 8 bytes <= FMHA_NOALLOC_SCRATCH_BYTES), before any HIP
+    call."""
+    import head_attention_forward_fmha_amd as fm
+    lib = fm.load_library()
+    header = open(os.path.join(ROOT, "include", "fmha.h")).read()
+    assert "#define FMHA_NOALLOC_SCRATCH_BYTES (16u << 20)" in header
+    assert fm.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # q, k, v, out, dout, lse, cu_q, cu_k, batch, tq, tk, mq, mk, heads, d, causal, scale,
+    # dq, dk, dv, stream
+    base = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, None, None, 1, 256, 256,
+            256, 256, 2, 128, 1, ctypes.c_float(0.088), 0x70000, 0x80000, 0x90000, None]
+    for i, bad, status in ((4, None, 1), (5, None, 1), (17, None, 1), (18, None, 1),
+                           (19, None, 1), (17, 0x70002, 1), (14, 96, 2), (15, 2, 1)):
+        b = list(base)
+        b[i] = bad
+        assert lib.fmha_bwd_noalloc(*b) == status, (i, bad)
+    # over the limit: 2^21 + 1 rows of one head, or 2 heads of 2^20 + 64 tokens
+    limit_rows = fm.NOALLOC_SCRATCH_BYTES // 8
+    for heads, tq in ((1, limit_rows + 1), (2, limit_rows // 2 + 64)):
+        b = list(base)
+        b[9], b[10], b[11], b[12], b[13], b[14] = tq, tq, tq, tq, heads, 64
+        assert lib.fmha_bwd_noalloc(*b) == 2, (heads, tq)
+    empty = [None] * 8 + [0, 0, 0, 0, 0, 2, 64, 0, ctypes.c_float(0.125)] + [None] * 4
+    assert lib.fmha_bwd_noalloc(*empty) == 0
+
+
+def test_bwd_noalloc_binding_reports_the_limit():
+    import torch
+    import head_attention_forward_fmha_amd as fm
+    rows = fm.NOALLOC_SCRATCH_BYTES // 8 // 64 + 1      # 64 heads: one token over the limit
+    q = torch.zeros(rows, 64, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(64, rows)
+    with pytest.raises(fm.FmhaError, match="scratch"):
+        fm.bwd_noalloc(q, q, q, q, q, lse, q, q, q)
 
 
 def test_splitkv_num_splits_choice():
