@@ -372,9 +372,25 @@ struct WaveTile {
   float m_run, l_run, c;
   float m_log2;          // e4m3: running anchor; e2m1: integer running maximum (exp2 units)
   int key_lo;            // keys before this are hidden (block-aligned fp4 tiles)
-  // per-lane LDS byte offsets of the operand reads within a stage's tile
+  // per-lane LDS byte offsets of the operand reads within a stage's tile: one
+  // per K step, and one per V read for d block 0. The swizzle only permutes
+  // chunk bits that the d block index occupies, so block db's offset is
+  // v_off0[r] ^ (kVBlockXor * db); voff() forms it where it is read (from a
+  // copy of the base the compiler cannot hoist), which keeps kVReads registers
+  // live instead of kVReads * kDBlocks.
+  static constexpr int kVBlockXor = kFp4 ? 16 : (kFp8 ? 32 : 64);
   int k_off[kKSteps];
-  int v_off[kVReads][kDBlocks];
+  int v_off0[kVReads];
+  __device__ __forceinline__ void v_bases(int (&b)[kVReads]) const {
+#pragma unroll
+    for (int r = 0; r < kVReads; ++r) {
+      b[r] = v_off0[r];
+      asm volatile("" : "+v"(b[r]));
+    }
+  }
+  __device__ __forceinline__ static int voff(const int (&b)[kVReads], int r, int db) {
+    return b[r] ^ (kVBlockXor * db);
+  }
   // HBM -> LDS copy
   i32x4 k_rsrc, v_rsrc;
   uint32_t k_stride, v_stride;
@@ -426,24 +442,22 @@ struct WaveTile {
     for (int t = 0; t < kKSteps; ++t)
       k_off[t] = col * kRowBytes + (((2 * t + half) ^ swz<kChunks>(col)) * 16);
 #pragma unroll
-    for (int r = 0; r < kVReads; ++r)
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) {
-        if constexpr (kFp4) {
-          const int row = 32 * half + 8 * (gi >> 2) + 4 * r + (gi & 3);
-          v_off[r][db] = row * kVRowBytes + ((db ^ swz<kVChunks>(row)) * 16) + 8 * (g & 1);
-        } else if constexpr (!kFp8) {
-          const int row = 8 * r + 4 * half + gi / 4;
-          const int d = 32 * db + 16 * (g & 1) + 4 * (gi & 3);
-          v_off[r][db] = row * kVRowBytes + (((d / 8) ^ swz<kVChunks>(row)) * 16) + (d % 8) * 2;
-        } else {
-          const int e = gi >> 1;
-          const int row = 8 * (e >> 2) + 4 * half + (e & 3);
-          const int byte_col = 32 * db + 16 * (g & 1) + 8 * (gi & 1);
-          v_off[r][db] =
-              row * kVRowBytes + (((byte_col / 16) ^ swz<kVChunks>(row)) * 16) + (byte_col % 16);
-        }
+    for (int r = 0; r < kVReads; ++r) {
+      if constexpr (kFp4) {
+        const int row = 32 * half + 8 * (gi >> 2) + 4 * r + (gi & 3);
+        v_off0[r] = row * kVRowBytes + ((0 ^ swz<kVChunks>(row)) * 16) + 8 * (g & 1);
+      } else if constexpr (!kFp8) {
+        const int row = 8 * r + 4 * half + gi / 4;
+        const int d = 16 * (g & 1) + 4 * (gi & 3);
+        v_off0[r] = row * kVRowBytes + (((d / 8) ^ swz<kVChunks>(row)) * 16) + (d % 8) * 2;
+      } else {
+        const int e = gi >> 1;
+        const int row = 8 * (e >> 2) + 4 * half + (e & 3);
+        const int byte_col = 16 * (g & 1) + 8 * (gi & 1);
+        v_off0[r] =
+            row * kVRowBytes + (((byte_col / 16) ^ swz<kVChunks>(row)) * 16) + (byte_col % 16);
       }
+    }
 
     // HBM -> LDS copy. Each wave copies 1 KB blocks: lane l lands at byte 16*l
     // of the block, so the swizzle is applied by choosing which global chunk
@@ -857,10 +871,12 @@ struct WaveTile {
       // supplies d row 32*db + m and keys 32*half + pi(0..31), and scales them
       // by the exponent of key block half, column d
       const unsigned char* vsc = (const unsigned char*)(vs + kVTileBytes) + half * kD + col;
+      int vb[kVReads];
+      v_bases(vb);
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
-        const auto lo = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + v_off[0][db]));
-        const auto hi = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + v_off[1][db]));
+        const auto lo = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + voff(vb, 0, db)));
+        const auto hi = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + voff(vb, 1, db)));
         const int sa = vsc[32 * db];
         const i32x8 a = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
         const i32x8 b = {pb4[0], pb4[1], pb4[2], pb4[3], 0, 0, 0, 0};
@@ -875,13 +891,15 @@ struct WaveTile {
       // registers the reads in flight take.
       constexpr int kN = (kBN / 16) * kDBlocks;   // MFMAs per tile
       constexpr int kAhead = 3;
+      int vb[kVReads];
+      v_bases(vb);
       bf16x8 va[kAhead + 1];
       auto read_v = [&](int i) {
         const int ks16 = i / kDBlocks, db = i % kDBlocks;
         bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(vs + v_off[0][db] + 16 * ks16 * kVRowBytes));
+            (LDS_AS bf16x4*)(vs + voff(vb, 0, db) + 16 * ks16 * kVRowBytes));
         bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(vs + v_off[1][db] + 16 * ks16 * kVRowBytes));
+            (LDS_AS bf16x4*)(vs + voff(vb, 1, db) + 16 * ks16 * kVRowBytes));
         va[i % (kAhead + 1)] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
 #pragma unroll
@@ -901,6 +919,8 @@ struct WaveTile {
       }
     } else {
       // all 64 keys of the tile in one e4m3 MFMA per d block
+      int vb[kVReads];
+      v_bases(vb);
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
         i32x8 a;
@@ -908,7 +928,7 @@ struct WaveTile {
         for (int r = 0; r < 4; ++r) {
           // read r delivers bytes 8r..8r+7: keys 32*(r>>1) + 16*(r&1) + ...
           const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (LDS_AS i32x2*)(vs + v_off[0][db] + (32 * (r >> 1) + 16 * (r & 1)) * kVRowBytes));
+              (LDS_AS i32x2*)(vs + voff(vb, 0, db) + (32 * (r >> 1) + 16 * (r & 1)) * kVRowBytes));
           a[2 * r] = t[0];
           a[2 * r + 1] = t[1];
         }
@@ -955,9 +975,9 @@ struct WaveTile {
     const int l = t / kDBlocks, db = t % kDBlocks;
     const int row0 = 16 * (2 * kH + l);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (LDS_AS bf16x4*)(vs + v_off[0][db] + row0 * kVRowBytes));
+        (LDS_AS bf16x4*)(vs + (v_off0[0] ^ (kVBlockXor * db)) + row0 * kVRowBytes));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (LDS_AS bf16x4*)(vs + v_off[1][db] + row0 * kVRowBytes));
+        (LDS_AS bf16x4*)(vs + (v_off0[1] ^ (kVBlockXor * db)) + row0 * kVRowBytes));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 
@@ -1111,6 +1131,72 @@ struct WaveTile {
       float lse = -__builtin_inff();
       if (l_run > 0.f) lse = (m_run * c + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
       p.lse_part[((size_t)split * p.heads + w.head) * p.total_q + w.q_start + qi] = lse;
+    }
+  }
+
+  // The epilogue with O written through LDS: each lane's O^T accumulators hold
+  // 4 consecutive d of one query per register group, so direct stores write 8
+  // bytes per lane into 32 different rows. Here the wave first places its
+  // rows' bf16 O, half of d at a time, into a 4 KB LDS region (four 1 KB
+  // blocks of 8 rows x 128 bytes at lds + r * kBlockStride, 16-byte chunks
+  // XOR-swizzled by (row >> 1) & 7, which leaves at most two lanes on a bank),
+  // then reads it back row-major, 16 bytes per lane, and stores 8 rows x 128
+  // contiguous bytes per instruction. The region must be one no other wave
+  // touches until this wave's later copies into it (the kernels pass blocks of
+  // a stage this wave itself refills). LSE as in epilogue().
+  template <int kBlockStride>
+  __device__ __forceinline__ void epilogue_lds(const FwdParams& p, const WorkItem& w,
+                                               uint32_t lds_addr) {
+    // the lane-dependent offsets below are formed here, after the tile loop:
+    // derived from a lane index the compiler cannot see before this point, so
+    // they are not hoisted into the loop, where registers are scarce
+    lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+    int ln = lane;
+    asm volatile("" : "+s"(lds_addr), "+v"(ln));
+    LDS_AS char* lds = (LDS_AS char*)(uintptr_t)lds_addr;
+    const int lcol = ln & 31, lhalf = ln >> 5;
+    l_run = wave_half_swap_sum(l_run);
+    const float num_scale = kFp8 ? p.v_scale[w.head] : 1.f;
+    const float inv_l = (l_run > 0.f && qi < w.sq) ? num_scale / l_run : 0.f;
+    const int row_stride = p.heads * kD;
+    static_assert(kD == 128, "the staging spans a 16 KB K stage: four 1 KB blocks per wave");
+    constexpr int kPasses = kD / 64;               // 64 d (128 bytes) per pass
+    auto sw = [](int row) { return (row >> 1) & 7; };
+    // this lane's write position: row col, block col / 8, row col % 8 inside it
+    LDS_AS char* wrow = lds + (lcol >> 3) * kBlockStride + (lcol & 7) * 128;
+    // this lane's read position: row R = 8 s + lane / 8 of block s, chunk lane % 8
+    const int rr = ln >> 3, rc = ln & 7;
+    bf16_t* out0 = (bf16_t*)p.out + (size_t)w.head * kD;
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+#pragma unroll
+      for (int dbp = 0; dbp < 2; ++dbp)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const int db = 2 * pass + dbp;
+          bf16x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (bf16_t)(oacc[db][4 * ig + e] * inv_l);
+          // d = 32 db + 8 ig + 4 half: 16-byte chunk 4 dbp + ig of the 128-byte row
+          *(LDS_AS bf16x4*)(wrow + (((4 * dbp + ig) ^ sw(lcol)) * 16) + 8 * lhalf) = o4;
+        }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int row = 8 * s + rr;               // row of this wave's 32
+        const bf16x8 v = *(const LDS_AS bf16x8*)(lds + s * kBlockStride + rr * 128 +
+                                                 ((rc ^ sw(row)) * 16));
+        if (wave_q0 + row < w.sq)
+          *(bf16x8*)(out0 + (size_t)(w.q_start + wave_q0 + row) * row_stride + 64 * pass +
+                     8 * rc) = v;
+      }
+    }
+    if (p.lse != nullptr && half == 0 && qi < w.sq) {
+      float lse = -__builtin_inff();
+      const float lsub = kFp8 ? kPScaleLog2 : 0.f;
+      const float mlog2 = (kFp4 || kFp8) ? m_log2 : m_run * c;
+      if (l_run > 0.f)
+        lse = (mlog2 + (__builtin_amdgcn_logf(l_run) - lsub)) * 0.69314718055994531f;
+      p.lse[(size_t)w.head * p.total_q + w.q_start + qi] = lse;
     }
   }
 

@@ -118,7 +118,14 @@ void fmha_fwd_kernel(FwdParams params) {
   }
   if (j < n_tiles) step(j, std::integral_constant<int, 0>());
 
+  // d = 128: O goes out through this wave's own blocks of K stage 1 (its four
+  // 1 KB blocks of that 16 KB stage): every wave's reads ended at the last
+  // barrier, and the next item writes them first by this wave's own copies of
+  // its tile 1. At d = 64 a stage holds only half the staging, so O is stored
+  // from registers.
   if constexpr (kSplit) t.epilogue_partial(p, w, split);
+  else if constexpr (kD == 128)
+    t.template epilogue_lds<1024 * kWaves4>(p, w, lds_address(&smem_k[1][1024 * wave]));
   else t.epilogue(p, w);
   };
   for_each_item<kCausal, kSplit>(params, run_item);
@@ -292,7 +299,16 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   if (j <= n) slot_pair(j, std::integral_constant<int, 0>());
   if (j + 1 <= n) slot_pair(j + 1, std::integral_constant<int, 1>());
 
+  // d = 128: O goes out through LDS blocks no other wave touches before this
+  // wave's own later copies (four 1 KB blocks of a 16 KB K stage per wave):
+  // group A uses its blocks of K stage 2 (first refilled after the next item's
+  // first barrier), group B its blocks of K stage 1 (refilled first by its own
+  // copies of the next item's tile 1). At d = 64 a stage holds only half the
+  // staging, so O is stored from registers.
   if constexpr (kSplit) t.epilogue_partial(p, w, split);
+  else if constexpr (kD == 128)
+    t.template epilogue_lds<1024 * 4>(p, w, grp == 0 ? lds_address(&smem_k[2][1024 * (wave & 3)])
+                                                     : lds_address(&smem_k[1][1024 * (wave & 3)]));
   else t.epilogue(p, w);
   };
   for_each_item<kCausal, kSplit>(params, run_item);
