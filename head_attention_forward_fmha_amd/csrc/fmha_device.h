@@ -303,10 +303,11 @@ __device__ __forceinline__ void for_each_item(const FwdParams& params, F&& f) {
     ItemCursor cursor(n_work_items<kSplit>(params));
     int item;
     // Items follow each other without a workgroup barrier: every tile loop
-    // ends behind an LDS barrier (all reads of its stages done) and epilogues
-    // touch no LDS, so the next item's first copies cannot overwrite anything
-    // still read, and the previous item's output stores drain while the next
-    // item's loads are in flight.
+    // ends behind an LDS barrier (all reads of its stages done), and an
+    // epilogue touches only LDS blocks that the same wave refills first, so
+    // the next item's first copies cannot overwrite anything still read, and
+    // the previous item's output stores drain while the next item's loads are
+    // in flight.
     while (cursor.next(item)) f(kernel_params(), item);
   } else {
     const int n_items = n_work_items<kSplit>(params);
@@ -373,63 +374,62 @@ struct WaveTile {
   float m_log2;          // e4m3: running anchor; e2m1: integer running maximum (exp2 units)
   int key_lo;            // keys before this are hidden (block-aligned fp4 tiles)
   // per-lane LDS byte offsets of the operand reads within a stage's tile: one
-  // per K step, and one per V read for d block 0. The swizzle only permutes
-  // chunk bits that the d block index occupies, so block db's offset is
-  // v_off0[r] ^ (kVBlockXor * db); voff() forms it where it is read (from a
-  // copy of the base the compiler cannot hoist), which keeps kVReads registers
-  // live instead of kVReads * kDBlocks.
+  // per K step, and one per V read and d block. The swizzle only permutes
+  // chunk bits that the d block index occupies, so block db's offset is block
+  // 0's ^ (kVBlockXor * db).
   static constexpr int kVBlockXor = kFp4 ? 16 : (kFp8 ? 32 : 64);
   int k_off[kKSteps];
-  int v_off0[kVReads];
-  __device__ __forceinline__ void v_bases(int (&b)[kVReads]) const {
-#pragma unroll
-    for (int r = 0; r < kVReads; ++r) {
-      b[r] = v_off0[r];
-      asm volatile("" : "+v"(b[r]));
-    }
-  }
-  __device__ __forceinline__ static int voff(const int (&b)[kVReads], int r, int db) {
-    return b[r] ^ (kVBlockXor * db);
-  }
+  int v_off[kVReads][kDBlocks];
   // HBM -> LDS copy
   i32x4 k_rsrc, v_rsrc;
   uint32_t k_stride, v_stride;
-  int k_voff[kLoadsPerWave], v_voff[kVLoadsPerWave];
+  // Per-lane offset of this wave's first copy instruction of a K (V) tile.
+  // Instruction r of the tile reads kCopyRowsK * r rows further on, a step the
+  // swizzle does not see (it reads only lower row bits), so its offset is
+  // k_copy0 + r * kCopyRowsK * k_stride: the difference is uniform and joins
+  // the tile's scalar offset.
+  static constexpr int kCopyRowsK = 1024 * kWaves / kRowBytes;
+  static constexpr int kCopyRowsV = 1024 * kWaves / kVRowBytes;
+  int k_copy0, v_copy0;
   const unsigned char* vs_base;  // e2m1 V exponents: (document start block, head), uniform
   uint32_t vs_stride;
   int vs_last, vs_lds_delta;      // last block (relative); image offset from lds_v0
 
+  // Sets up one wave for work item w: rows 32*row_chunk .. +31 of the item's
+  // block, copies split over kWaves waves with this one at index `wave`.
   __device__ __forceinline__ void init(const FwdParams& p, const WorkItem& w, int wave,
                                        int row_chunk) {
+    init_lanes(p);
+    begin_rows(w, row_chunk);
+    load_q(p, w, qi);
+    init_read_offsets();
+    init_strides(p);
+    set_copy_source(p, w);
+    init_copy_offsets(wave);
+  }
+
+  // What stays the same for every work item of a launch: lane identity, the
+  // operand read offsets within a stage, the per-lane copy offsets.
+  __device__ __forceinline__ void init_wave(const FwdParams& p, int wave) {
+    init_lanes(p);
+    init_read_offsets();
+    init_strides(p);
+    init_copy_offsets(wave);
+  }
+  __device__ __forceinline__ void init_lanes(const FwdParams& p) {
     lane = threadIdx.x & 63;
     col = lane & 31;
     half = lane >> 5;
     g = lane >> 4;
     gi = lane & 15;
-    wave_q0 = w.m0 + 32 * row_chunk;
-    qi = wave_q0 + col;
     c = p.scale_log2;
-    m_run = -__builtin_inff();
-    m_log2 = -__builtin_inff();
-    l_run = 0.f;
-    key_lo = w.key_lo;
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-
-    // Q: the B operand of S^T = K Q^T, held in registers for the whole loop
-    {
-      const int row_stride = p.heads * kD;
-      const int qrow = w.q_start + min(qi, w.sq - 1);
-      const bf16_t* qp = (const bf16_t*)p.q + (size_t)qrow * row_stride + w.head * kD + 8 * half;
-#pragma unroll
-      for (int t = 0; t < kKSteps; ++t) qreg[t] = *(const bf16x8*)(qp + 16 * t);
-      // The kernels wait for Q (vmcnt 0) before their tile loops, after issuing
-      // their first K/V copies, so the two HBM round trips overlap and no wait
-      // on the stream's counter is ever needed for Q inside the loop.
-    }
-
+  }
+  __device__ __forceinline__ void init_strides(const FwdParams& p) {
+    k_stride = (uint32_t)p.heads * kRowBytes;
+    v_stride = (uint32_t)p.heads * kVRowBytes;
+    if constexpr (kFp4) vs_stride = (uint32_t)p.heads * kD;
+  }
+  __device__ __forceinline__ void init_read_offsets() {
     // operand read offsets. K rows 32*kb + col at logical chunk 2t + half.
     // bf16 V (tr16): rows 16*ks16 + 8r + 4*half + gi/4, d = 32*db + 16*(g&1) + 4*(gi&3).
     // fp8 V (tr8): rows 32*(r>>1) + 16*(r&1) + 8*(e>>2) + 4*half + (e&3), e = gi/2,
@@ -445,57 +445,100 @@ struct WaveTile {
     for (int r = 0; r < kVReads; ++r) {
       if constexpr (kFp4) {
         const int row = 32 * half + 8 * (gi >> 2) + 4 * r + (gi & 3);
-        v_off0[r] = row * kVRowBytes + ((0 ^ swz<kVChunks>(row)) * 16) + 8 * (g & 1);
+        v_off[r][0] = row * kVRowBytes + ((0 ^ swz<kVChunks>(row)) * 16) + 8 * (g & 1);
       } else if constexpr (!kFp8) {
         const int row = 8 * r + 4 * half + gi / 4;
         const int d = 16 * (g & 1) + 4 * (gi & 3);
-        v_off0[r] = row * kVRowBytes + (((d / 8) ^ swz<kVChunks>(row)) * 16) + (d % 8) * 2;
+        v_off[r][0] = row * kVRowBytes + (((d / 8) ^ swz<kVChunks>(row)) * 16) + (d % 8) * 2;
       } else {
         const int e = gi >> 1;
         const int row = 8 * (e >> 2) + 4 * half + (e & 3);
         const int byte_col = 16 * (g & 1) + 8 * (gi & 1);
-        v_off0[r] =
+        v_off[r][0] =
             row * kVRowBytes + (((byte_col / 16) ^ swz<kVChunks>(row)) * 16) + (byte_col % 16);
       }
+#pragma unroll
+      for (int db = 1; db < kDBlocks; ++db) v_off[r][db] = v_off[r][0] ^ (kVBlockXor * db);
     }
+  }
 
-    // HBM -> LDS copy. Each wave copies 1 KB blocks: lane l lands at byte 16*l
-    // of the block, so the swizzle is applied by choosing which global chunk
-    // each lane fetches. Offsets are relative to this (document, head); rows
-    // past the document end fall outside the buffer and arrive as zeros.
-    k_stride = (uint32_t)p.heads * kRowBytes;
-    v_stride = (uint32_t)p.heads * kVRowBytes;
+  // HBM -> LDS copy. Each wave copies 1 KB blocks: lane l lands at byte 16*l
+  // of the block, so the swizzle is applied by choosing which global chunk
+  // each lane fetches. Offsets are relative to the item's (document, head);
+  // rows past the document end fall outside the buffer and arrive as zeros.
+  __device__ __forceinline__ void init_copy_offsets(int wave) {
+    {
+      const int byte = 1024 * wave + 16 * lane;
+      const int row = byte / kRowBytes;
+      const int phys = (byte % kRowBytes) / 16;
+      k_copy0 = row * (int)k_stride + (phys ^ swz<kChunks>(row)) * 16;
+    }
+    {
+      const int byte = 1024 * wave + 16 * lane;
+      const int row = byte / kVRowBytes;
+      const int phys = (byte % kVRowBytes) / 16;
+      v_copy0 = row * (int)v_stride + (phys ^ swz<kVChunks>(row)) * 16;
+    }
+    if constexpr (kFp4) {
+      static_assert(!kFp4 || kD == 128, "the exponent image is [2][128]");
+      vs_lds_delta = kVTileBytes - 1024 * wave;
+    }
+  }
+
+  // The row state of work item w: this wave's rows, an empty running softmax,
+  // O = 0. Everything the item's softmax and epilogue read.
+  __device__ __forceinline__ void begin_rows(const WorkItem& w, int row_chunk) {
+    wave_q0 = w.m0 + 32 * row_chunk;
+    qi = wave_q0 + col;
+    m_run = -__builtin_inff();
+    m_log2 = -__builtin_inff();
+    l_run = 0.f;
+    key_lo = w.key_lo;
+    if constexpr (kFp4) key_lo = __builtin_amdgcn_readfirstlane(key_lo);
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  }
+
+  // The copy state of work item w (buffer descriptors of its K and V, the e2m1
+  // exponent rows) and the loads of its Q rows: everything the item's copies
+  // and Q.K^T read. A kernel may call this for the next item once the current
+  // one has issued its last copy and run its last Q.K^T.
+  __device__ __forceinline__ void begin_copies(const FwdParams& p, const WorkItem& w,
+                                               int row_chunk) {
+    load_q(p, w, w.m0 + 32 * row_chunk + col);
+    set_copy_source(p, w);
+  }
+  // Q: the B operand of S^T = K Q^T, held in registers for the item's tile
+  // loop; this lane's row is `row` of the document (clamped to its last row)
+  __device__ __forceinline__ void load_q(const FwdParams& p, const WorkItem& w, int row) {
+    {
+      const int row_stride = p.heads * kD;
+      const int qrow = w.q_start + min(row, w.sq - 1);
+      const bf16_t* qp = (const bf16_t*)p.q + (size_t)qrow * row_stride + w.head * kD + 8 * half;
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t) qreg[t] = *(const bf16x8*)(qp + 16 * t);
+      // The kernels wait for Q (vmcnt 0) before their tile loops, after issuing
+      // their first K/V copies, so the two HBM round trips overlap and no wait
+      // on the stream's counter is ever needed for Q inside the loop.
+    }
+  }
+  __device__ __forceinline__ void set_copy_source(const FwdParams& p, const WorkItem& w) {
     k_rsrc = make_buffer_rsrc((const char*)p.k + (size_t)w.k_start * k_stride + w.head * kRowBytes,
                               (uint32_t)w.sk * k_stride);
     v_rsrc = make_buffer_rsrc((const char*)p.v + (size_t)w.k_start * v_stride + w.head * kVRowBytes,
                               (uint32_t)w.sk * v_stride);
-#pragma unroll
-    for (int r = 0; r < kLoadsPerWave; ++r) {
-      const int byte = 1024 * (r * kWaves + wave) + 16 * lane;
-      const int row = byte / kRowBytes;
-      const int phys = (byte % kRowBytes) / 16;
-      k_voff[r] = row * (int)k_stride + (phys ^ swz<kChunks>(row)) * 16;
-    }
-#pragma unroll
-    for (int r = 0; r < kVLoadsPerWave; ++r) {
-      const int byte = 1024 * (r * kWaves + wave) + 16 * lane;
-      const int row = byte / kVRowBytes;
-      const int phys = (byte % kVRowBytes) / 16;
-      v_voff[r] = row * (int)v_stride + (phys ^ swz<kVChunks>(row)) * 16;
-    }
     // e2m1 V exponents: a tile's two 32-key blocks are rows k_start/32 + 2j and
     // + 2j + 1 of [blocks, heads, kD]; lane l copies bytes 4l .. 4l + 3 of the
     // tile's [2][kD] image (block half, d = 4*col .. 4*col + 3). A block past
     // the end of the array (only in a tile's masked tail, whose V codes read
     // as zeros) is replaced by the last block, so every read stays in bounds.
     if constexpr (kFp4) {
-      static_assert(!kFp4 || kD == 128, "the exponent image is [2][128]");
-      vs_stride = (uint32_t)p.heads * kD;
       const int blk0 = w.k_start / 32;
       const int n_blocks = (p.total_k + 31) / 32;
       vs_base = p.v_mx_scale + (size_t)blk0 * vs_stride + (size_t)w.head * kD;
       vs_last = max(n_blocks - 1 - blk0, 0);
-      vs_lds_delta = kVTileBytes - 1024 * wave;
     }
   }
 
@@ -525,7 +568,6 @@ struct WaveTile {
           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b));
       vs_stride = __builtin_amdgcn_readfirstlane(vs_stride);
       vs_last = __builtin_amdgcn_readfirstlane(vs_last);
-      key_lo = __builtin_amdgcn_readfirstlane(key_lo);
     }
   }
 
@@ -536,15 +578,20 @@ struct WaveTile {
   // the raw-buffer range check that turns rows past the document end into
   // zeros is made on the per-lane offset, so every byte of the copy is checked
   // against the buffer's size.
+  // `base` is a copy of k_copy0 (v_copy0) made where the tile's copy starts,
+  // opaque to the compiler, so that the per-instruction sums are formed here
+  // and not hoisted out of the tile loop into registers of their own.
   template <int kStage, int kR>
-  __device__ __forceinline__ void copy_k_one(int j, uint32_t lds_k0) {
+  __device__ __forceinline__ void copy_k_one(int j, uint32_t lds_k0, int base) {
     lds_dma_16<kStage * kTileBytes + 1024 * kWaves * kR>(
-        lds_k0, k_voff[kR] + scalar_offset((int)((uint32_t)(j * kBN) * k_stride)), k_rsrc, 0);
+        lds_k0, base + scalar_offset((int)((uint32_t)(j * kBN + kR * kCopyRowsK) * k_stride)),
+        k_rsrc, 0);
   }
   template <int kStage, int kR>
-  __device__ __forceinline__ void copy_v_one(int j, uint32_t lds_v0) {
+  __device__ __forceinline__ void copy_v_one(int j, uint32_t lds_v0, int base) {
     lds_dma_16<kStage * kVStageBytes + 1024 * kWaves * kR>(
-        lds_v0, v_voff[kR] + scalar_offset((int)((uint32_t)(j * kBN) * v_stride)), v_rsrc, 0);
+        lds_v0, base + scalar_offset((int)((uint32_t)(j * kBN + kR * kCopyRowsV) * v_stride)),
+        v_rsrc, 0);
   }
   // e2m1 V: tile j's exponent image (the same 256 bytes from every wave)
   template <int kStage>
@@ -556,14 +603,18 @@ struct WaveTile {
   }
   template <int kStage>
   __device__ __forceinline__ void copy_k(int j, uint32_t lds_k0) {
+    int base = k_copy0;
+    asm volatile("" : "+v"(base));
     [&]<int... kR>(std::integer_sequence<int, kR...>) {
-      (copy_k_one<kStage, kR>(j, lds_k0), ...);
+      (copy_k_one<kStage, kR>(j, lds_k0, base), ...);
     }(std::make_integer_sequence<int, kLoadsPerWave>());
   }
   template <int kStage>
   __device__ __forceinline__ void copy_v(int j, uint32_t lds_v0) {
+    int base = v_copy0;
+    asm volatile("" : "+v"(base));
     [&]<int... kR>(std::integer_sequence<int, kR...>) {
-      (copy_v_one<kStage, kR>(j, lds_v0), ...);
+      (copy_v_one<kStage, kR>(j, lds_v0, base), ...);
     }(std::make_integer_sequence<int, kVLoadsPerWave>());
     if constexpr (kFp4) copy_v_scales<kStage>(j, lds_v0);
   }
@@ -623,26 +674,28 @@ struct WaveTile {
     if constexpr (kFp4) need_mask = need_mask || (kt0 < key_lo);
     if (need_mask) {
       const int lim = kCausal ? min(sk - 1, qi + causal_off) : sk - 1;
-      if constexpr (kFp4) {
-        // visible iff key_lo <= key <= lim, as one unsigned compare per key
-        const uint32_t n_vis = (uint32_t)max(lim - key_lo + 1, 0);
-        const int base = kt0 + 4 * half - key_lo;
-#pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rel = base + 32 * kb + (i / 4) * 8 + (i % 4);
-            if ((uint32_t)rel >= n_vis) sacc[kb][i] = -__builtin_inff();
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt0 + 32 * kb + (i / 4) * 8 + 4 * half + (i % 4);
-            if (key > lim) sacc[kb][i] = -__builtin_inff();
-          }
-      }
+      // Element (kb, i) holds key kt0 + 4*half + off with the constant
+      // off = 32 kb + 8 (i/4) + i%4: each test compares that constant with a
+      // per-row bound, opaque to the compiler, and selects -inf; a scheduling
+      // barrier after each element keeps its compare next to its select. Left
+      // to the compiler, the tests are grouped with one scalar register pair
+      // per lane mask, or folded into per-element sums kept in registers
+      // across the tile loop.
+      int hi_rel = lim - kt0 - 4 * half;   // visible iff off <= hi_rel
+      [[maybe_unused]] int lo_rel = key_lo - kt0 - 4 * half;   // fp4: and off >= lo_rel
+      asm volatile("" : "+v"(hi_rel), "+v"(lo_rel));
+      auto mask_one = [&](auto e_tag) __attribute__((always_inline)) {
+        constexpr int e = decltype(e_tag)::value;
+        constexpr int kb = e / 16, i = e % 16;
+        constexpr int off = 32 * kb + 8 * (i / 4) + (i % 4);
+        bool hidden = off > hi_rel;
+        if constexpr (kFp4) hidden = hidden || off < lo_rel;
+        if (hidden) sacc[kb][i] = -__builtin_inff();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      [&]<int... kE>(std::integer_sequence<int, kE...>) {
+        (mask_one(std::integral_constant<int, kE>()), ...);
+      }(std::make_integer_sequence<int, 16 * kKeyBlocks>());
     }
     if constexpr (kFp4) {
       softmax_fp4();
@@ -871,12 +924,10 @@ struct WaveTile {
       // supplies d row 32*db + m and keys 32*half + pi(0..31), and scales them
       // by the exponent of key block half, column d
       const unsigned char* vsc = (const unsigned char*)(vs + kVTileBytes) + half * kD + col;
-      int vb[kVReads];
-      v_bases(vb);
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
-        const auto lo = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + voff(vb, 0, db)));
-        const auto hi = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + voff(vb, 1, db)));
+        const auto lo = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + v_off[0][db]));
+        const auto hi = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS i32x2*)(vs + v_off[1][db]));
         const int sa = vsc[32 * db];
         const i32x8 a = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
         const i32x8 b = {pb4[0], pb4[1], pb4[2], pb4[3], 0, 0, 0, 0};
@@ -891,15 +942,13 @@ struct WaveTile {
       // registers the reads in flight take.
       constexpr int kN = (kBN / 16) * kDBlocks;   // MFMAs per tile
       constexpr int kAhead = 3;
-      int vb[kVReads];
-      v_bases(vb);
       bf16x8 va[kAhead + 1];
       auto read_v = [&](int i) {
         const int ks16 = i / kDBlocks, db = i % kDBlocks;
         bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(vs + voff(vb, 0, db) + 16 * ks16 * kVRowBytes));
+            (LDS_AS bf16x4*)(vs + v_off[0][db] + 16 * ks16 * kVRowBytes));
         bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4*)(vs + voff(vb, 1, db) + 16 * ks16 * kVRowBytes));
+            (LDS_AS bf16x4*)(vs + v_off[1][db] + 16 * ks16 * kVRowBytes));
         va[i % (kAhead + 1)] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
 #pragma unroll
@@ -919,8 +968,6 @@ struct WaveTile {
       }
     } else {
       // all 64 keys of the tile in one e4m3 MFMA per d block
-      int vb[kVReads];
-      v_bases(vb);
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
         i32x8 a;
@@ -928,7 +975,7 @@ struct WaveTile {
         for (int r = 0; r < 4; ++r) {
           // read r delivers bytes 8r..8r+7: keys 32*(r>>1) + 16*(r&1) + ...
           const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (LDS_AS i32x2*)(vs + voff(vb, 0, db) + (32 * (r >> 1) + 16 * (r & 1)) * kVRowBytes));
+              (LDS_AS i32x2*)(vs + v_off[0][db] + (32 * (r >> 1) + 16 * (r & 1)) * kVRowBytes));
           a[2 * r] = t[0];
           a[2 * r + 1] = t[1];
         }
@@ -975,9 +1022,9 @@ struct WaveTile {
     const int l = t / kDBlocks, db = t % kDBlocks;
     const int row0 = 16 * (2 * kH + l);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (LDS_AS bf16x4*)(vs + (v_off0[0] ^ (kVBlockXor * db)) + row0 * kVRowBytes));
+        (LDS_AS bf16x4*)(vs + v_off[0][db] + row0 * kVRowBytes));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (LDS_AS bf16x4*)(vs + (v_off0[1] ^ (kVBlockXor * db)) + row0 * kVRowBytes));
+        (LDS_AS bf16x4*)(vs + v_off[1][db] + row0 * kVRowBytes));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 
@@ -1142,8 +1189,9 @@ struct WaveTile {
   // XOR-swizzled by (row >> 1) & 7, which leaves at most two lanes on a bank),
   // then reads it back row-major, 16 bytes per lane, and stores 8 rows x 128
   // contiguous bytes per instruction. The region must be one no other wave
-  // touches until this wave's later copies into it (the kernels pass blocks of
-  // a stage this wave itself refills). LSE as in epilogue().
+  // touches meanwhile: the 4-wave kernel passes blocks of a K stage this wave
+  // itself refills first, the 8-wave kernel a private block per wave. LSE as
+  // in epilogue().
   template <int kBlockStride>
   __device__ __forceinline__ void epilogue_lds(const FwdParams& p, const WorkItem& w,
                                                uint32_t lds_addr) {

@@ -181,6 +181,35 @@ struct StampTrace {
   }
 };
 
+// One work item as the ping-pong kernel runs it: the decoded (document, head,
+// query block), its share of the key tiles under split-KV, the number of key
+// tiles n, and the causal offset; n < 0 for an item with no query rows.
+struct ItemPlan {
+  WorkItem w;
+  int split, n, causal_off;
+};
+
+template <bool kCausal, bool kSplit, bool kFp4>
+__device__ __forceinline__ ItemPlan plan_item(const FwdParams& p, int item, int bm) {
+  ItemPlan it;
+  it.split = 0;
+  if constexpr (kSplit) {
+    it.split = item % p.num_splits;
+    item /= p.num_splits;
+  }
+  it.w = decode_work_item(p, bm, item);
+  it.n = -1;
+  it.causal_off = 0;
+  if (it.w.m0 >= it.w.sq) return it;
+  if constexpr (kFp4) align_keys_to_blocks(it.w);
+  it.causal_off = it.w.sk - it.w.sq;
+  int kend = it.w.sk;
+  if (kCausal) kend = min(it.w.sk, max(0, it.w.m0 + bm + it.causal_off));
+  it.n = (kend + kBN - 1) / kBN;
+  if constexpr (kSplit) it.n = take_split(it.w, it.causal_off, it.n, it.split, p.num_splits);
+  return it;
+}
+
 template <int kD, bool kCausal, int kPv, bool kSplit, typename Trace = NoPhaseTrace>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves8 * 64, kWaves8 * 64),
                           amdgpu_waves_per_eu(2, 2)))
@@ -188,130 +217,226 @@ void fmha_fwd_pingpong_kernel(FwdParams params) {
   // each group of 4 waves copies whole tiles, so the tile math is set up for 4
   // copying waves
   using WT = WaveTile<kD, kCausal, kPv, 4>;
+  // d = 128 stores O through a private 4 KB LDS block per wave (epilogue_lds);
+  // d = 64 and split-KV partials store from registers
+  constexpr bool kStageO = kD == 128 && !kSplit;
   __shared__ __attribute__((aligned(1024))) char smem_k[kStages8][WT::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char smem_v[kStages8][WT::kVStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_o[kStageO ? kWaves8 * 4096 : 1024];
 
+  // The wave index is uniform over the wave; readfirstlane says so, which
+  // makes every branch on the group a scalar branch (taken as a divergent one,
+  // both groups' paths would share one wave's register allocation).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Trace trace;
-  trace.begin(params, threadIdx.x >> 6);
-
-  auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
-  trace.mark(kEvItem);
-  int split = 0;
-  if constexpr (kSplit) {
-    split = item % p.num_splits;
-    item /= p.num_splits;
-  }
-  WorkItem w = decode_work_item(p, kBM8, item);
-  if (w.m0 >= w.sq) return;  // uniform over the workgroup
-  if constexpr (WT::kFp4) align_keys_to_blocks(w);
-  int causal_off = w.sk - w.sq;
-  int kend = w.sk;
-  if (kCausal) kend = min(w.sk, max(0, w.m0 + kBM8 + causal_off));
-  int n = (kend + kBN - 1) / kBN;
-  if constexpr (kSplit) n = take_split(w, causal_off, n, split, p.num_splits);
-
-  const int wave = threadIdx.x >> 6;
+  trace.begin(params, wave);
   const int grp = wave >> 2;  // 0: group A, 1: group B (half a tile behind)
   // 32-row chunks alternate between the groups, which evens out the causal work
-  WT t;
-  t.init(p, w, wave & 3, 2 * (wave & 3) + grp);
-  if constexpr (kCausal || WT::kFp4) t.pin_copy_state();
+  const int row_chunk = 2 * (wave & 3) + grp;
   const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * (wave & 3)]);
   const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * (wave & 3)]);
 
-  // Schedule. Tile j lives in stage j % 3. Slot 2j: group A runs the MFMA phase
-  // of tile j (Q.K^T of tile j, P.V of tile j-1) while group B runs the VALU
-  // phase of tile j-1 (mask, softmax, P); slot 2j+1 swaps the roles. Copies are
-  // issued only at the start of VALU phases, one group at a time: group B
-  // copies K of tile j+2 in slot 2j (its stage's previous K was last read in
-  // slot 2j-1), group A copies V of tile j+1 in slot 2j+1 (last read in slot
-  // 2j-1). Each group waits for its previous copies at the end of its VALU
-  // phase, so tile j's K and V are visible from slot 2j-1 and 2j on.
-  // The MFMA phase runs at raised wave priority, so that when both waves of a
-  // SIMD have an instruction ready the MFMA issues first and the VALU work of
-  // the other group fills the cycles in between.
-  auto mfma_phase = [&](int j, auto r_tag) {
-    constexpr int r = decltype(r_tag)::value;  // j % 3
-    __builtin_amdgcn_s_setprio(2);
-    if (j < n && t.active(j, causal_off)) t.qk(smem_k[r]);
-    trace.mark(kEvQkDone);
-    if (j >= 1 && t.active(j - 1, causal_off)) t.pv(smem_v[(r + 2) % 3]);
-    __builtin_amdgcn_s_setprio(0);
-    trace.mark(kEvMfmaDone);
-  };
-  auto valu_phase = [&](int j) {
-    if (j >= 0 && j < n && t.active(j, causal_off)) t.softmax(j, w.sk, causal_off);
-  };
+  // The workgroup's items, skipping those without query rows (uniform over the
+  // workgroup). Causal launches are persistent and walk the XCD's share with an
+  // ItemCursor, re-reading the parameters per item (kernel_params); the others
+  // run the single item their block index names.
+  // Each group runs its own copy of the item loop (kGrp): the two follow the
+  // same sequence of barriers, and neither's values are live in the other's
+  // code, which a branch on the group inside one loop would make them.
+  auto run_group = [&](auto g_tag) __attribute__((always_inline)) {
+    constexpr int kGrp = decltype(g_tag)::value;
+    ItemCursor cursor(kCausal ? n_work_items<kSplit>(params) : 0);
+    bool single_pending = true;
+    auto next_plan = [&](ItemPlan& it) __attribute__((always_inline)) -> bool {
+      if constexpr (kCausal) {
+        int item;
+        while (cursor.next(item)) {
+          it = plan_item<kCausal, kSplit, WT::kFp4>(kernel_params(), item, kBM8);
+          if (it.n >= 0) return true;
+        }
+        return false;
+      } else {
+        if (!single_pending) return false;
+        single_pending = false;
+        const int n_items = n_work_items<kSplit>(params);
+        const int xcd = blockIdx.x % kXcds;
+        const int per = n_items / kXcds, extra = n_items % kXcds;
+        it = plan_item<kCausal, kSplit, WT::kFp4>(
+            params, xcd * per + min(xcd, extra) + (int)blockIdx.x / kXcds, kBM8);
+        return it.n >= 0;
+      }
+    };
+    auto item_params = [&]() -> const FwdParams& {
+      if constexpr (kCausal) return kernel_params();
+      return params;
+    };
 
-  auto slot_pair = [&](int j, auto r_tag) {
-    constexpr int r = decltype(r_tag)::value;  // j % 3
-    // ---- slot 2j
-    if (grp == 0) {
-      mfma_phase(j, r_tag);
+    ItemPlan cur;
+    if (!next_plan(cur)) return;
+    trace.mark(kEvItem);
+    WT t;
+    t.init(item_params(), cur.w, wave & 3, row_chunk);
+    if constexpr (kCausal || WT::kFp4) t.pin_copy_state();
+    // first item's prologue: K tiles 0 and 1 and V tile 0
+    if constexpr (kGrp == 0) {
+      if (cur.n > 0) t.template copy_k<0>(0, k_lds0);
+      if (cur.n > 0) t.template copy_v<0>(0, v_lds0);
     } else {
-      const bool copy = j + 2 < n;
-      if (copy) t.template copy_k<(r + 2) % 3>(j + 2, k_lds0);
-      trace.mark(kEvCopyIssued);
-      valu_phase(j - 1);
-      trace.mark(kEvValuDone);
-      // the copies of K tile j+1 (issued in slot 2j-2) have landed
-      if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      if (cur.n > 1) t.template copy_k<1>(1, k_lds0);
     }
-    trace.mark(kEvWaitDone);
-    lds_barrier();
-    trace.mark(kEvSlot);
-    // ---- slot 2j+1
-    if (grp == 0) {
-      const bool copy = j + 1 < n;
-      if (copy) t.template copy_v<(r + 1) % 3>(j + 1, v_lds0);
-      trace.mark(kEvCopyIssued);
-      valu_phase(j);
-      trace.mark(kEvValuDone);
-      // the copies of V tile j (issued in slot 2j-1) have landed
-      if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kVCopyOps));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    } else {
-      mfma_phase(j, r_tag);
+
+    for (;;) {
+      const int n = cur.n, causal_off = cur.causal_off, sk = cur.w.sk;
+      // Schedule. Tile j lives in stage j % 3. Slot 2j: group A runs the MFMA phase
+      // of tile j (Q.K^T of tile j, P.V of tile j-1) while group B runs the VALU
+      // phase of tile j-1 (mask, softmax, P); slot 2j+1 swaps the roles. Copies are
+      // issued only at the start of VALU phases, one group at a time: group B
+      // copies K of tile j+2 in slot 2j (its stage's previous K was last read in
+      // slot 2j-1), group A copies V of tile j+1 in slot 2j+1 (last read in slot
+      // 2j-1). Each group waits for its previous copies at the end of its VALU
+      // phase, so tile j's K and V are visible from slot 2j-1 and 2j on.
+      // The MFMA phase runs at raised wave priority, so that when both waves of a
+      // SIMD have an instruction ready the MFMA issues first and the VALU work of
+      // the other group fills the cycles in between.
+      auto mfma_phase = [&](int j, auto r_tag) {
+        constexpr int r = decltype(r_tag)::value;  // j % 3
+        __builtin_amdgcn_s_setprio(2);
+        if (j < n && t.active(j, causal_off)) t.qk(smem_k[r]);
+        trace.mark(kEvQkDone);
+        if (j >= 1 && t.active(j - 1, causal_off)) t.pv(smem_v[(r + 2) % 3]);
+        __builtin_amdgcn_s_setprio(0);
+        trace.mark(kEvMfmaDone);
+      };
+      auto valu_phase = [&](int j) {
+        if (j >= 0 && j < n && t.active(j, causal_off)) t.softmax(j, sk, causal_off);
+      };
+
+      auto slot_pair = [&](int j, auto r_tag) {
+        constexpr int r = decltype(r_tag)::value;  // j % 3
+        // ---- slot 2j
+        if constexpr (kGrp == 0) {
+          mfma_phase(j, r_tag);
+        } else {
+          const bool copy = j + 2 < n;
+          if (copy) t.template copy_k<(r + 2) % 3>(j + 2, k_lds0);
+          trace.mark(kEvCopyIssued);
+          valu_phase(j - 1);
+          trace.mark(kEvValuDone);
+          // the copies of K tile j+1 (issued in slot 2j-2) have landed
+          if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        trace.mark(kEvWaitDone);
+        lds_barrier();
+        trace.mark(kEvSlot);
+        // ---- slot 2j+1
+        if constexpr (kGrp == 0) {
+          const bool copy = j + 1 < n;
+          if (copy) t.template copy_v<(r + 1) % 3>(j + 1, v_lds0);
+          trace.mark(kEvCopyIssued);
+          valu_phase(j);
+          trace.mark(kEvValuDone);
+          // the copies of V tile j (issued in slot 2j-1) have landed
+          if (copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kVCopyOps));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        } else {
+          mfma_phase(j, r_tag);
+        }
+        trace.mark(kEvWaitDone);
+        lds_barrier();
+        trace.mark(kEvSlot);
+      };
+
+      // the item's Q and first copies have landed (for a later item: issued
+      // during the previous item's last slot pair and epilogue)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      lds_barrier();
+      trace.mark(kEvSlot);
+      int j = 0;
+      for (; j + 3 <= n; j += 3) {
+        slot_pair(j, std::integral_constant<int, 0>());
+        slot_pair(j + 1, std::integral_constant<int, 1>());
+        slot_pair(j + 2, std::integral_constant<int, 2>());
+      }
+      if (j < n) slot_pair(j, std::integral_constant<int, 0>());
+      if (j + 1 < n) slot_pair(j + 1, std::integral_constant<int, 1>());
+
+      // The last slot pair, j = n, runs P.V of tile n-1 (and group B's softmax of
+      // it). Every copy of this item has landed (each group waited for its last
+      // ones in slot 2n-2 or 2n-1) and no K stage is read again, so the next
+      // item's Q loads and its K tiles 0 and 1 are issued now and land under
+      // this pair and the epilogue; its V tile 0 follows the pair's last barrier,
+      // after which no V stage is read. Nothing in this pair waits for them.
+      ItemPlan nxt;
+      bool more = false;
+      if constexpr (kCausal) {
+        more = next_plan(nxt);
+        if (!more) nxt = cur;
+        // The descriptors switch unconditionally (to the current item's when
+        // there is no next one): switched under the branch, the merged values
+        // would no longer be known to be uniform and the copies could not take
+        // them from scalar registers.
+        t.set_copy_source(kernel_params(), nxt.w);
+        t.pin_copy_state();
+        if (more) {
+          t.load_q(kernel_params(), nxt.w, nxt.w.m0 + 32 * row_chunk + t.col);
+          if constexpr (kGrp == 0) {
+            if (nxt.n > 0) t.template copy_k<0>(0, k_lds0);
+          } else {
+            if (nxt.n > 1) t.template copy_k<1>(1, k_lds0);
+          }
+        }
+      }
+      {
+        const char* vs = smem_v[(n + 2) % 3];  // tile n-1's V stage
+        const bool pv_last = n >= 1 && t.active(n - 1, causal_off);
+        // ---- slot 2n
+        if constexpr (kGrp == 0) {
+          __builtin_amdgcn_s_setprio(2);
+          trace.mark(kEvQkDone);
+          if (pv_last) t.pv(vs);
+          __builtin_amdgcn_s_setprio(0);
+          trace.mark(kEvMfmaDone);
+        } else {
+          trace.mark(kEvCopyIssued);
+          valu_phase(n - 1);
+          trace.mark(kEvValuDone);
+        }
+        trace.mark(kEvWaitDone);
+        lds_barrier();
+        trace.mark(kEvSlot);
+        // ---- slot 2n+1
+        if constexpr (kGrp == 0) {
+          trace.mark(kEvCopyIssued);
+          trace.mark(kEvValuDone);
+        } else {
+          __builtin_amdgcn_s_setprio(2);
+          trace.mark(kEvQkDone);
+          if (pv_last) t.pv(vs);
+          __builtin_amdgcn_s_setprio(0);
+          trace.mark(kEvMfmaDone);
+        }
+        trace.mark(kEvWaitDone);
+        lds_barrier();
+        trace.mark(kEvSlot);
+      }
+      if constexpr (kCausal) {
+        if (kGrp == 0 && more && nxt.n > 0) t.template copy_v<0>(0, v_lds0);
+      }
+
+      if constexpr (kSplit) t.epilogue_partial(item_params(), cur.w, cur.split);
+      else if constexpr (kStageO)
+        t.template epilogue_lds<1024>(item_params(), cur.w, lds_address(&smem_o[4096 * wave]));
+      else t.epilogue(item_params(), cur.w);
+
+      if (!more) break;
+      cur = nxt;
+      trace.mark(kEvItem);
+      t.begin_rows(cur.w, row_chunk);
     }
-    trace.mark(kEvWaitDone);
-    lds_barrier();
-    trace.mark(kEvSlot);
   };
-
-  // prologue: K tiles 0 and 1 and V tile 0
-  if (grp == 0) {
-    if (n > 0) t.template copy_k<0>(0, k_lds0);
-    if (n > 0) t.template copy_v<0>(0, v_lds0);
-  } else {
-    if (n > 1) t.template copy_k<1>(1, k_lds0);
-  }
-  // the first copies and Q (issued by init) have landed
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  lds_barrier();
-  trace.mark(kEvSlot);
-  int j = 0;
-  for (; j + 3 <= n + 1; j += 3) {
-    slot_pair(j, std::integral_constant<int, 0>());
-    slot_pair(j + 1, std::integral_constant<int, 1>());
-    slot_pair(j + 2, std::integral_constant<int, 2>());
-  }
-  if (j <= n) slot_pair(j, std::integral_constant<int, 0>());
-  if (j + 1 <= n) slot_pair(j + 1, std::integral_constant<int, 1>());
-
-  // d = 128: O goes out through LDS blocks no other wave touches before this
-  // wave's own later copies (four 1 KB blocks of a 16 KB K stage per wave):
-  // group A uses its blocks of K stage 2 (first refilled after the next item's
-  // first barrier), group B its blocks of K stage 1 (refilled first by its own
-  // copies of the next item's tile 1). At d = 64 a stage holds only half the
-  // staging, so O is stored from registers.
-  if constexpr (kSplit) t.epilogue_partial(p, w, split);
-  else if constexpr (kD == 128)
-    t.template epilogue_lds<1024 * 4>(p, w, grp == 0 ? lds_address(&smem_k[2][1024 * (wave & 3)])
-                                                     : lds_address(&smem_k[1][1024 * (wave & 3)]));
-  else t.epilogue(p, w);
-  };
-  for_each_item<kCausal, kSplit>(params, run_item);
+  if (grp == 0) run_group(std::integral_constant<int, 0>());
+  else run_group(std::integral_constant<int, 1>());
 }
 
 // ---------------------------------------------------------------- pipelined kernel
