@@ -138,6 +138,13 @@ def parse_args():
                          "WRITE_SIZE) of a --counters run into an entry of the traffic file")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="print a rocprofv3 --stats kernel_stats.csv as a text table")
+    ap.add_argument("--summarize-sq", metavar="COUNTER_CSV",
+                    help="print the SQ/GRBM counters of a --counters run per FMHA launch, with "
+                         "the MFMA FLOP, exp2 and MFMA-busy checks against the workload")
+    ap.add_argument("--sustain", type=float, default=None, metavar="SECONDS",
+                    help="after the warm-up, run the step back to back for SECONDS and print "
+                         "one line (launches, us per step, TFLOP/s): a load under which the "
+                         "board's clock and power can be read (amd-smi metric -p -c)")
     ap.add_argument("--microbench", action="store_true",
                     help="instead of a step: instruction-throughput microbenchmarks (exp2, FMA, "
                          "P conversions, MFMA, LDS reads and their overlap), one JSON line")
@@ -399,6 +406,83 @@ def summarize_counters(fetch_csv, write_csv, copy_bytes=256 * 1024 * 1024):
     return out
 
 
+def run_sustained(w, step, seconds, warmup):
+    """The step back to back for `seconds` (synchronising every 50 steps)."""
+    import time
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, t0 = 0, time.time()
+    e0.record()
+    while time.time() - t0 < seconds:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+        n += 50
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    print(json.dumps({"workload": w.name, "sustained_s": round(time.time() - t0, 1), "steps": n,
+                      "us_per_step": round(ms * 1e3, 1),
+                      "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1)}), flush=True)
+
+
+def visible_scores(w):
+    """Score elements the method evaluates an exp2 for: per (document, head),
+    the (query, key) pairs the mask leaves visible (bottom-right causal)."""
+    import numpy as np
+    total = 0
+    for sq, sk in w.doc_lens:
+        if w.causal:
+            i = np.arange(sq, dtype=np.int64)
+            total += int(np.clip(i + 1 + sk - sq, 0, sk).sum())
+        else:
+            total += sq * sk
+    return total * w.heads
+
+
+def summarize_sq(csv_path, w, simds=1024, xcds=8):
+    """Per-launch averages of the counters of a rocprofv3 --pmc --counters run
+    for the FMHA kernel, and three checks against the workload:
+    MFMA FLOP = 512 x the MFMA MOPS counters, against the counted FLOP (the
+    kernel also multiplies the masked part of its diagonal tiles);
+    transcendental instructions x 64 lanes per visible score (one exp2 per
+    score, plus the rescale exp2s and the epilogue's log);
+    MFMA busy cycles per SIMD over the elapsed cycles per XCD (GRBM_GUI_ACTIVE
+    sums the XCDs)."""
+    per = {}
+    for r in _counter_rows(csv_path):
+        if "fmha_fwd" not in r["Kernel_Name"]:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        d = per.setdefault(key, {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{csv_path}: no FMHA dispatches")
+    names = sorted({k[1] for k in per})
+    counters = sorted({c for d in per.values() for c in d})
+    avg = {c: sum(d.get(c, 0.0) for d in per.values()) / len(per) for c in counters}
+    lines = [f"{len(per)} dispatches of {', '.join(names)}"]
+    for c in counters:
+        lines.append(f"  {c:32s} {avg[c]:.4e}")
+    mops = sum(v for c, v in avg.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    if mops:
+        lines.append(f"  MFMA FLOP (512 x MOPS)           {512 * mops:.4e}  "
+                     f"= {512 * mops / w.flops():.4f} x the counted {w.flops():.4e}")
+    if "SQ_INSTS_VALU_TRANS_F32" in avg:
+        vis = visible_scores(w)
+        lines.append(f"  transcendental lane ops / visible score  "
+                     f"{64 * avg['SQ_INSTS_VALU_TRANS_F32'] / vis:.4f}  ({vis:.4e} visible scores)")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+        elapsed = avg["GRBM_GUI_ACTIVE"] / xcds
+        lines.append(f"  MFMA busy per SIMD / elapsed     {busy:.4e} / {elapsed:.4e} = "
+                     f"{busy / elapsed:.3f}")
+    return "\n".join(lines)
+
+
 def summarize_trace(stats_csv):
     rows = _counter_rows(stats_csv)
     lines = [f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
@@ -456,6 +540,11 @@ def main():
     args = parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_sq:
+        from synthetic import EXTRA_WORKLOADS, WORKLOADS
+        w = {**WORKLOADS, **EXTRA_WORKLOADS}[SHORT.get(args.workload, args.workload)]
+        print(summarize_sq(args.summarize_sq, w))
         return
     if args.summarize_counters:
         # the counters must have been taken on the current sources: the entry is
@@ -527,6 +616,9 @@ def main():
         return
     if args.trace:
         run_trace(w, d, step, args)
+        return
+    if args.sustain is not None:
+        run_sustained(w, step, args.sustain, args.warmup)
         return
     total_ms, each = time_steps(step, args.steps, args.warmup)
     if args.step != "fwd":
