@@ -1047,10 +1047,15 @@ struct WaveTile {
     const int k0 = 32 * u;
     const bool need = (k0 + 32 > sk) || (kCausal && (k0 + 31 > wave_q0 + causal_off));
     if (need) {
+      // constants against one per-row bound, as in softmax()
       const int lim = kCausal ? min(sk - 1, qi + causal_off) : sk - 1;
+      int hi_rel = lim - k0 - 4 * half;
+      asm volatile("" : "+v"(hi_rel));
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (k0 + 8 * (i / 4) + 4 * half + (i % 4) > lim) s[i] = -__builtin_inff();
+      for (int i = 0; i < 16; ++i) {
+        if (8 * (i / 4) + (i % 4) > hi_rel) s[i] = -__builtin_inff();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
