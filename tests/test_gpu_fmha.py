@@ -7,7 +7,9 @@ sum is taken before P is rounded to e4m3). That bar alone passes an all-zero O
 on long rows (|O| is about 0.01 there), so fp8 outputs are also held to the
 method's own quantised result (``oracle.attention_fp8pv_emulated``) at the
 bf16 bar, widened only by the oracle's fp32-ambiguity and subnormal-band
-allowances.
+allowances. In the small-document edge cases (not c5) an fp8 element may also
+exceed the stated bar by no more than the method's own pinned rounding bound
+plus the bf16 bar: rows with a few keys can, by the method itself.
 
 Every check also reports the error normalised by the row RMS of O_ref and
 holds it to a derived bar (tests/parity.py), which stays sharp on long rows.
@@ -67,14 +69,24 @@ def _run(inp, causal, scale, heads, d, fp8=False, max_q=None, max_k=None, varian
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def _check(o, lse, o_ref, lse_ref, fp8=False, what="", emu=None):
+def _check(o, lse, o_ref, lse_ref, fp8=False, what="", emu=None, stated_fp8_bar=True):
     """The stated bar against the exact oracle; the normalised error against the
     exact oracle (bf16) or against the emulated method ``emu`` (fp8, rows in
-    o's row order after reshaping to [rows, d])."""
+    o's row order after reshaping to [rows, d]).
+
+    fp8 edge cases (``stated_fp8_bar=False``): on a row with a handful of
+    visible keys the method's own rounding of P to e4m3 (each weight within
+    2^-4) can move O past the stated absolute term (pinned on the CPU in
+    tests/test_oracle_fp8.py); there an element also passes within the
+    oracle's bound on that rounding plus the bf16 bar. Every row is still held
+    to the emulated method at the bf16 bar. The c5 workload, the configuration
+    the fp8 bar is stated for, is held to the stated bar alone."""
     atol, rtol = (O_ATOL_FP8, O_RTOL_FP8) if fp8 else (O_ATOL, O_RTOL)
     assert not np.isnan(o).any(), f"{what}: NaN in O (unwritten or invalid output)"
     err = np.abs(o - o_ref)
     tol = atol + rtol * np.abs(o_ref)
+    if fp8 and not stated_fp8_bar:
+        tol = np.maximum(tol, emu.bound.reshape(o.shape) + O_ATOL + O_RTOL * np.abs(o_ref))
     bad = err > tol
     if bad.any():
         idx = np.unravel_index(np.argmax(err - tol), err.shape)
@@ -123,7 +135,7 @@ def _full_parity(lens, heads, d, causal, seed=0, scale=None, fp8=False, max_q=No
                                               inp.cu_k, causal, scale)
     else:
         o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, causal, scale)
-    _check(o, lse, o_ref, lse_ref, fp8=fp8, emu=emu,
+    _check(o, lse, o_ref, lse_ref, fp8=fp8, emu=emu, stated_fp8_bar=False,
            what=f"lens={lens} h={heads} d={d} causal={causal} variant={variant}")
     return inp, o, lse
 
@@ -265,6 +277,35 @@ def test_many_small_documents(variant):
     lens = tuple((int(x), int(x)) for x in rng.integers(0, 200, 40))
     for causal in (False, True):
         _full_parity(lens, 4, 128, causal, seed=11, variant=variant)
+
+
+def _edge_mix(n_random, max_len, seed):
+    """Documents for a persistent launch with more work items than the grid
+    holds (every workgroup walks several items, so each item's loads are
+    issued under the previous item's end): random lengths mixed with a
+    single-token document, key-less and query-less documents, sq < sk and
+    sq > sk under bottom-right causal alignment, and tails just past a tile."""
+    rng = np.random.default_rng(seed)
+    edge = ((1, 1), (10, 0), (0, 12), (13, 40), (40, 13), (257, 257), (65, 65), (0, 0))
+    rand = tuple((int(x), int(x)) for x in rng.integers(1, max_len, n_random))
+    mixed = list(rand)
+    for i, e in enumerate(edge):
+        mixed.insert((7 * i + 3) % (len(mixed) + 1), e)
+    return tuple(mixed)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("variant", ["four_wave", "pingpong"])
+def test_persistent_items_with_edge_documents(d, variant):
+    # 40 documents x 16 heads x 3 blocks of 256 rows: far more items than the
+    # 256 workgroups of the persistent grid, empty ones included
+    lens = _edge_mix(32, 600, seed=21)
+    _full_parity(lens, 16, d, True, seed=22, variant=variant)
+
+
+def test_fp8_persistent_items_with_edge_documents():
+    lens = _edge_mix(22, 400, seed=23)
+    _full_parity(lens, 12, 128, True, fp8=True, seed=24, variant="pingpong")
 
 
 @pytest.mark.parametrize("variant", VARIANTS_FP8)

@@ -125,6 +125,18 @@ def test_fp4_many_small_documents(variant):
         _full_parity(lens, 2, causal, seed=23, variant=variant)
 
 
+def test_fp4_persistent_items_with_edge_documents():
+    """More work items than the persistent grid holds (each workgroup walks
+    several, loading the next under the current one's end), with documents
+    that start inside a 32-token block, key-less and query-less documents,
+    sq != sk, and a single-token document among random lengths."""
+    rng = np.random.default_rng(25)
+    lens = [(int(x), int(x)) for x in rng.integers(1, 400, 22)]
+    for i, e in enumerate(((1, 1), (10, 0), (0, 12), (13, 40), (40, 13), (257, 257), (33, 33))):
+        lens.insert((5 * i + 2) % (len(lens) + 1), e)
+    _full_parity(tuple(lens), 12, True, seed=26, variant="pingpong")
+
+
 @pytest.mark.parametrize("variant", VARIANTS_FP4)
 def test_fp4_large_scores_and_scale(variant):
     # a large softmax scale gives peaked rows, groups far below the row maximum

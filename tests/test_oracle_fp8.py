@@ -287,14 +287,46 @@ def test_zero_or_wrong_head_output_fails_the_long_row_check():
     assert ((emu.ambiguity + emu.slack) / bar).max() < 0.5
 
 
+def test_method_can_exceed_the_stated_bar_on_a_few_key_row():
+    """A counterexample to the stated fp8 bar holding on every short row: the
+    third query of a 242-token causal document (three visible keys) in the
+    mixed-length edge case of the GPU parity tests (seed 24, 12 heads). The
+    method's own rounding of the three weights to e4m3 moves element 14 of head
+    10 by 0.053 from the exact attention, past 5e-2 + 5e-2 |O| = 0.0505, and
+    within the oracle's bound on that rounding (which is what the GPU check
+    allows there, besides holding the kernel to the emulated method)."""
+    rng = np.random.default_rng(23)
+    edge = ((1, 1), (10, 0), (0, 12), (13, 40), (40, 13), (257, 257), (65, 65), (0, 0))
+    lens = [(int(x), int(x)) for x in rng.integers(1, 400, 22)]
+    for i, e in enumerate(edge):
+        lens.insert((7 * i + 3) % (len(lens) + 1), e)
+    inp = make_inputs(tuple(lens), 12, 128, seed=24, fp8_pv=True)
+    b = 8
+    assert lens[b] == (242, 242) and int(inp.cu_q[b]) == 916
+    sq = slice(int(inp.cu_q[b]), int(inp.cu_q[b + 1]))
+    sk = slice(int(inp.cu_k[b]), int(inp.cu_k[b + 1]))
+    q, k, v8 = inp.q[sq], inp.k[sk], inp.v_e4m3[sk]
+    cu = np.array([0, 242])
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    o, _ = oracle.attention_fp8pv(q, k, v8, inp.v_scale, cu, cu, True, scale)
+    emu = oracle.attention_fp8pv_emulated(q, k, v8, inp.v_scale, cu, cu, True, scale)
+    row = 2 * 12 + 10
+    err = abs(emu.out[row, 14] - o[2, 10, 14])
+    assert err > 5e-2 + 5e-2 * abs(o[2, 10, 14])
+    assert err <= emu.bound[row, 14] + 1e-12
+    # the relaxed GPU tolerance covers it with room to spare
+    assert err <= emu.bound[row, 14] + 1e-2 + 1e-2 * abs(o[2, 10, 14])
+
+
 @pytest.mark.parametrize("lens,causal", [
     (((200, 200),), True), (((129, 129), (64, 64)), False), (((100, 300), (300, 100)), True),
     (((600, 600), (1, 1)), True), (((200, 200), (77, 77), (129, 129)), True),
 ])
 def test_method_meets_the_stated_bar_on_short_rows(lens, causal):
     """With the first tile's largest key mapped exactly, the method's own P
-    rounding keeps short rows (one key, a few keys whose V cancel) within the
-    stated fp8 bar 5e-2 + 5e-2 |O| of the exact attention, and within its bound."""
+    rounding keeps these cases' short rows (one key, a few keys whose V cancel)
+    within the stated fp8 bar 5e-2 + 5e-2 |O| of the exact attention, and
+    within its bound (not every short row: see the counterexample above)."""
     inp = make_inputs(lens, 2, 128, seed=13, fp8_pv=True)
     scale = float(np.float32(1.0 / np.sqrt(128)))
     o, _ = oracle.attention_fp8pv(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q, inp.cu_k,
