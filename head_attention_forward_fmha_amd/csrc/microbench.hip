@@ -62,6 +62,30 @@ __device__ __forceinline__ float softmax_like(float (&x)[32], int iters) {
   return l;
 }
 
+// 2^x on the FMA path, for comparing a polynomial exp2 with v_exp_f32 (which
+// shares the quarter-rate unit with the P conversions). Cody and Waite's range
+// reduction: x = n + f with n = round(x) and |f| <= 1/2, rounding by adding and
+// subtracting 1.5 * 2^23 (n then sits in the low mantissa bits of the sum); 2^f
+// by a degree-3 polynomial fitted here for relative error on [-1/2, 1/2] (max
+// 7.5e-5, about 13.7 bits, evaluated in fp32: more than the 8 bits a bf16 P
+// keeps); 2^n by adding n to the exponent field. x is clamped at -125, so that
+// the result stays a normal number (the polynomial's value lies in [0.7, 1.42]).
+// Eight vector instructions: max, add, sub, sub, three FMAs, shift-and-add (in
+// this benchmark a ninth: the compiler quiets a possible NaN with another max,
+// since each chain feeds a value built by integer addition back in).
+__device__ __forceinline__ float exp2_poly(float x) {
+  constexpr float kRound = 12582912.f;   // 1.5 * 2^23
+  x = __builtin_fmaxf(x, -125.f);
+  const float t = x + kRound;
+  const float n = t - kRound;
+  const float f = x - n;
+  const float p = __builtin_fmaf(
+      __builtin_fmaf(__builtin_fmaf(0.05517132207751274f, f, 0.24261054396629333f), f,
+                     0.6932609677314758f),
+      f, 0.9999281167984009f);
+  return __builtin_bit_cast(float, __builtin_bit_cast(int, p) + (__builtin_bit_cast(int, t) << 23));
+}
+
 template <int kWhich>
 __global__ __launch_bounds__(1024) void microbench_kernel(Slot* out, int iters, int mfma_waves) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
@@ -80,7 +104,38 @@ __global__ __launch_bounds__(1024) void microbench_kernel(Slot* out, int iters, 
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   unsigned long long t_stop = 0;  // set by waves timed over part of their loop
 
-  if constexpr (kWhich == FMHA_MB_EXP2 || kWhich == FMHA_MB_FMA) {
+  if constexpr (kWhich == FMHA_MB_EXP2_POLY) {
+    float x[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) x[c] = 0.01f * (lane + c);
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) x[c] = exp2_poly(-__builtin_fabsf(x[c]));
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) sink += x[c];
+  } else if constexpr (kWhich == FMHA_MB_EXP2_WITH_FMA) {
+    // one op: one v_exp_f32 and four v_fma_f32, each on its own chain
+    float x[kChains], y[kChains][4];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+      x[c] = 0.01f * (lane + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[c][j] = 0.02f * (lane + c + j);
+    }
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) {
+          x[c] = __builtin_amdgcn_exp2f(-__builtin_fabsf(x[c]));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[c][j] = __builtin_fmaf(y[c][j], 0.999f, 0.001f);
+        }
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) sink += x[c] + y[c][0] + y[c][1] + y[c][2] + y[c][3];
+  } else if constexpr (kWhich == FMHA_MB_EXP2 || kWhich == FMHA_MB_FMA) {
     float x[kChains];
 #pragma unroll
     for (int c = 0; c < kChains; ++c) x[c] = 0.01f * (lane + c);
@@ -252,6 +307,8 @@ double ops_per_iteration(int which) {
     case FMHA_MB_CVT_E4M3:
     case FMHA_MB_CVT_E2M1:
     case FMHA_MB_EXP2_E4M3:
+    case FMHA_MB_EXP2_POLY:
+    case FMHA_MB_EXP2_WITH_FMA:
       return 8.0 * kChains;
     case FMHA_MB_MFMA_BF16:
     case FMHA_MB_MFMA_E4M3:
@@ -293,6 +350,10 @@ hipError_t launch_any(int which, Slot* out, int grid, int wps, int iters, int mf
     case FMHA_MB_MFMA_WITH_VALU:
       return launch<FMHA_MB_MFMA_WITH_VALU>(out, grid, wps, iters, mfma_waves, s);
     case FMHA_MB_SOFTMAX: return launch<FMHA_MB_SOFTMAX>(out, grid, wps, iters, mfma_waves, s);
+    case FMHA_MB_EXP2_POLY:
+      return launch<FMHA_MB_EXP2_POLY>(out, grid, wps, iters, mfma_waves, s);
+    case FMHA_MB_EXP2_WITH_FMA:
+      return launch<FMHA_MB_EXP2_WITH_FMA>(out, grid, wps, iters, mfma_waves, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = ("fmha_microbench_run",)
 BENCHMARKS = {
     "exp2": 0, "fma": 1, "cvt_bf16": 2, "cvt_e4m3": 3, "cvt_e2m1": 4, "exp2_e4m3": 5,
     "mfma_bf16": 6, "mfma_e4m3": 7, "lds_b128": 8, "mfma_lds_b128": 9, "mfma_with_valu": 10,
-    "softmax": 11,
+    "softmax": 11, "exp2_poly": 12, "exp2_with_fma": 13,
 }
 MFMA_FLOP = {"mfma_bf16": 2 * 32 * 32 * 16, "mfma_e4m3": 2 * 32 * 32 * 64,
              "mfma_lds_b128": 2 * 32 * 32 * 16, "mfma_with_valu": 2 * 32 * 32 * 16}
@@ -73,6 +73,8 @@ PLAN = (
     ("lds_b128", 1, 400), ("lds_b128", 2, 400),
     ("mfma_lds_b128", 1, 400), ("mfma_lds_b128", 2, 400),
     ("mfma_with_valu", 2, 400),
+    ("exp2_poly", 1, 2000), ("exp2_poly", 2, 2000),
+    ("exp2_with_fma", 1, 2000), ("exp2_with_fma", 2, 2000),
 )
 
 

@@ -42,7 +42,12 @@ extern "C" {
                                      waves_per_simd must be 2                   */
 #define FMHA_MB_SOFTMAX 11      /* that softmax-like vector stream alone; one
                                    op = one iteration (32 scores)               */
-#define FMHA_MB_COUNT 12
+#define FMHA_MB_EXP2_POLY 12     /* 2^x on the FMA path: range reduction and a
+                                   degree-3 polynomial, 8 vector instructions;
+                                   one op = one 2^x                             */
+#define FMHA_MB_EXP2_WITH_FMA 13 /* one op = 1 v_exp_f32 + 4 v_fma_f32 on
+                                   independent chains                           */
+#define FMHA_MB_COUNT 14
 
 /*
  * Run benchmark `which` on the current HIP device: one warm-up launch, then
@@ -54,9 +59,10 @@ extern "C" {
  *   iters           1 .. 2^20 loop iterations
  *   result          host array of 2 doubles, written on success:
  *                   [0] median over the device's waves of cycles per
- *                       instruction (per op for FMHA_MB_EXP2_E4M3 and
- *                       FMHA_MB_SOFTMAX; for FMHA_MB_MFMA_WITH_VALU, of the
- *                       MFMA waves)
+ *                       instruction (per op for FMHA_MB_EXP2_E4M3,
+ *                       FMHA_MB_SOFTMAX, FMHA_MB_EXP2_POLY and
+ *                       FMHA_MB_EXP2_WITH_FMA; for FMHA_MB_MFMA_WITH_VALU, of
+ *                       the MFMA waves)
  *                   [1] FMHA_MB_MFMA_WITH_VALU: median cycles per iteration
  *                       of the vector waves' stream; otherwise 0
  *
