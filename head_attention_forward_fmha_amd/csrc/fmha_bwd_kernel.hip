@@ -16,14 +16,17 @@
 //      dP^T = V dO^T by rows, dQ^T += K^T dS^T transposed. Holding each
 //      query's dO row, it also computes D and LSE * log2(e) per (row, head)
 //      and writes them to the workspace;
-//   2. dK/dV: a workgroup owns 128 keys of one (document, head), 32 per wave,
-//      with K and V held in registers, and streams the document's 64-row Q and
-//      dO tiles through a three-stage LDS ring. It is the forward's structure with
-//      the roles of queries and keys swapped: S = Q K^T and dP = dO V^T read the
-//      streamed tiles by rows (lane = key, registers = queries), and
-//      dV^T += dO^T P and dK^T += Q^T dS read them transposed (ds_read_b64_tr_b16),
-//      with P and dS as the register operand, exactly as O^T += V^T P^T;
-//      it reads D and LSE * log2(e) of each query tile from the workspace.
+//   2. dK/dV: a workgroup owns 128 keys of one (document, head), 32 per wave
+//      position, and streams the document's 64-row Q and dO tiles through a
+//      three-stage LDS ring. It is the forward's structure with the roles of
+//      queries and keys swapped: S = Q K^T and dP = dO V^T read the streamed
+//      tiles by rows (lane = key, registers = queries), and dV^T += dO^T P and
+//      dK^T += Q^T dS read them transposed (ds_read_b64_tr_b16), with P and dS
+//      as the register operand, exactly as O^T += V^T P^T. Two groups of 4 waves
+//      split the work, one computing S, dP, P and dS (holding K and V), the other
+//      the transposed products (holding dV and dK), with P and dS passed
+//      through LDS; it reads D and LSE * log2(e) of each query tile from the
+//      workspace.
 //
 // Every output element is written by exactly one lane with a fixed summation
 // order, so the result is deterministic (no atomics); the price is that S and dP
@@ -178,260 +181,274 @@ __device__ __forceinline__ void store_bf16_rows(bf16_t* row, const f32x16* acc, 
 
 // ---------------------------------------------------------------- dK and dV
 
+// The dK/dV pass as two groups of 4 waves, two waves per SIMD: 128 keys per
+// workgroup, 32 per wave position (sub = wave % 4) as above, but the products
+// are split between the groups. Group A holds the position's K and V and turns
+// each query tile into S and dP (Q K^T, dO V^T by rows) and from them P and dS;
+// group B holds the dV and dK accumulators and runs the transposed products
+// dV^T += dO^T P, dK^T += Q^T dS. P and dS pass through LDS (8 KB per position
+// and tile). Step s, two barriers:
+//   phase 1: A runs S/dP of tile s; B issues the copies of tile s+1 and loads
+//            P/dS of tile s-1;
+//   phase 2: B runs dV/dK of tile s-1; A computes P/dS of tile s and stores
+//            them; B waits for its copies.
+// So each SIMD's matrix core is fed by one group at a time while the other
+// group's vector work, copies and LDS traffic run beside it, and each group
+// needs well under 256 registers where one wave holding everything needed 472
+// (one wave per SIMD). Q/dO tiles go through a ring of three stages: in step s
+// A reads tile s by rows, B reads tile s-1 transposed, and tile s+1 lands.
 template <int kD, bool kCausal>
-__global__ __attribute__((amdgpu_flat_work_group_size(kBwdWaves * 64, kBwdWaves * 64),
-                          amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(2 * kBwdWaves * 64, 2 * kBwdWaves * 64),
+                          amdgpu_waves_per_eu(2, 2)))
 void fmha_bwd_dkdv_kernel(BwdParams p) {
   using G = TileGeom<kD>;
-  // a ring of three stages: one barrier per tile (see the tile loop)
   __shared__ __attribute__((aligned(1024))) char smem_q[3][G::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char smem_do[3][G::kTileBytes];
   __shared__ __attribute__((aligned(16))) float smem_rows[3][2 * kTileRows];  // LSE*log2e, D
+  // P and dS of one tile per wave position: lane l's 16-byte chunk k (P of
+  // 16-query steps 0..3, then dS of steps 0..3) at 1024 k + 16 l, so each LDS
+  // access of a wave covers 1 KB contiguously
+  __shared__ __attribute__((aligned(1024))) char smem_pds[kBwdWaves][8 * 1024];
 
   const BwdItem w = decode_bwd_item(p, xcd_item(p.batch * p.heads * p.n_blocks), false, kCausal);
   const int n0 = w.block * kBwdRows;
   if (n0 >= w.sk) return;   // uniform over the workgroup
-  const int wave = threadIdx.x >> 6;
+  // readfirstlane: branches on the group are scalar branches, and each group's
+  // path gets its own register allocation
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2, sub = wave & 3;
   const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
-  const int kw0 = n0 + 32 * wave;   // this wave's first key (in the document)
+  const int kw0 = n0 + 32 * sub;   // this position's first key (in the document)
   const int causal_off = w.sk - w.sq;
   const uint32_t stride = (uint32_t)p.heads * G::kRowBytes;
-  const float c = p.scale_log2;
-
-  // K and V rows of this lane's key: the B operands of S = Q K^T and dP = dO V^T
-  bf16x8 kreg[G::kKSteps], vreg[G::kKSteps];
-  {
-    const size_t krow = (size_t)(w.k_start + min(kw0 + col, w.sk - 1)) * p.heads * kD +
-                        (size_t)w.head * kD + 8 * half;
-#pragma unroll
-    for (int t = 0; t < G::kKSteps; ++t) {
-      kreg[t] = *(const bf16x8*)((const bf16_t*)p.k + krow + 16 * t);
-      vreg[t] = *(const bf16x8*)((const bf16_t*)p.v + krow + 16 * t);
-    }
-  }
-  f32x16 dvacc[G::kDBlocks], dkacc[G::kDBlocks];
-#pragma unroll
-  for (int db = 0; db < G::kDBlocks; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dvacc[db][i] = dkacc[db][i] = 0.f;
-
-  TileLane<kD> tl;
-  tl.init(lane, wave, stride);
-  const i32x4 q_rsrc = make_buffer_rsrc(
-      (const char*)p.q + (size_t)w.q_start * stride + w.head * G::kRowBytes, (uint32_t)w.sq * stride);
-  const i32x4 do_rsrc = make_buffer_rsrc(
-      (const char*)p.dout + (size_t)w.q_start * stride + w.head * G::kRowBytes,
-      (uint32_t)w.sq * stride);
-  const uint32_t q_lds0 = lds_address(&smem_q[0][1024 * wave]);
-  const uint32_t do_lds0 = lds_address(&smem_do[0][1024 * wave]);
-  const uint32_t rows_lds0 = lds_address(&smem_rows[0][0]);
-  const size_t row_base = (size_t)w.head * p.total_q + w.q_start;
-
-  // query tiles: causal blocks start at the first query that sees key n0
   const int n_qt = (w.sq + kTileRows - 1) / kTileRows;
+  // causal blocks start at the first query tile that sees key n0
   const int t0 = kCausal ? max(0, n0 - causal_off) / kTileRows : 0;
-
-  // a tile's copies: Q and dO rows, then LSE*log2e and D of its 64 rows (every
-  // wave fetches the same 512 bytes: one 4-byte load per lane for each)
-  constexpr int kOps = 2 * G::kLoads + 2;
-  auto copy_tile = [&](int jt, auto stage_tag) {
-    constexpr int st = decltype(stage_tag)::value;
-    tl.template copy<st * G::kTileBytes>(q_lds0, q_rsrc, jt * kTileRows, stride);
-    tl.template copy<st * G::kTileBytes>(do_lds0, do_rsrc, jt * kTileRows, stride);
-    const size_t r = row_base + min(jt * kTileRows + lane, w.sq - 1);
-    const uint32_t rl = __builtin_amdgcn_readfirstlane(rows_lds0 + st * 2 * kTileRows * 4);
-    lds_dma_global_4(rl, p.lse2 + r);
-    lds_dma_global_4(rl + kTileRows * 4, p.delta + r);
+  // tile jt contributes to this position iff some query of it sees its first key
+  auto active = [&](int jt) {
+    return !kCausal || jt * kTileRows + kTileRows - 1 + causal_off >= kw0;
   };
+  LDS_AS char* pds_lds = (LDS_AS char*)(uintptr_t)lds_address(&smem_pds[sub][0]);
 
-  // One query tile (64 rows) against this wave's 32 keys, software-pipelined
-  // within the wave, since no other wave on the SIMD hides its vector work: S
-  // and dP of query block 0; then S and dP of block 1 interleaved with block 0's
-  // P and dS; then block 1's P and dS interleaved with the dV/dK products that
-  // need only block 0 (16-query steps 0 and 1); then the other products. kMask:
-  // the tile needs the causal mask or the query tail; it is chosen outside, so
-  // that no branch splits the interleaved stream.
-  auto compute = [&](int jt, auto stage_tag, auto mask_tag) {
-    constexpr int st = decltype(stage_tag)::value;
-    constexpr bool kMask = decltype(mask_tag)::value;
-    const char* qs = smem_q[st];
-    const char* dos = smem_do[st];
-    const float* rows = smem_rows[st];
-    const int q0 = jt * kTileRows;
-    const int key = kw0 + col;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
-    bf16x8 pb[4], dsb[4];
-
-    // S = Q K^T and dP = dO V^T of query block kb: rows 32*kb + 8(r/4) +
-    // 4*half + r%4 of the tile by this lane's key, operands two steps ahead of
-    // their MFMAs (a ring of three)
-    auto sdp = [&](auto kb_tag) {
-      constexpr int kb = decltype(kb_tag)::value;
-      constexpr int kAhead = 2;
-      bf16x8 qa[kAhead + 1], da[kAhead + 1];
-      auto read_rows = [&](int t) {
-        const int off = tl.row_off[t] + kb * 32 * G::kRowBytes;
-        qa[t % (kAhead + 1)] = *(const bf16x8*)(qs + off);
-        da[t % (kAhead + 1)] = *(const bf16x8*)(dos + off);
-      };
-#pragma unroll
-      for (int t = 0; t < kAhead; ++t) read_rows(t);
+  auto run_a = [&]() __attribute__((always_inline)) {
+    const float c = p.scale_log2;
+    bf16x8 kreg[G::kKSteps], vreg[G::kKSteps];
+    {
+      const size_t krow = (size_t)(w.k_start + min(kw0 + col, w.sk - 1)) * p.heads * kD +
+                          (size_t)w.head * kD + 8 * half;
 #pragma unroll
       for (int t = 0; t < G::kKSteps; ++t) {
-        if (t + kAhead < G::kKSteps) read_rows(t + kAhead);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t % (kAhead + 1)], kreg[t], s[kb], 0,
-                                                        0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t % (kAhead + 1)], vreg[t], dp[kb], 0,
-                                                         0, 0);
+        kreg[t] = *(const bf16x8*)((const bf16_t*)p.k + krow + 16 * t);
+        vreg[t] = *(const bf16x8*)((const bf16_t*)p.v + krow + 16 * t);
       }
-    };
-    // LSE*log2e and D of the 16 queries of block kb this lane's registers hold
-    auto read_rowvals = [&](int kb, float (&lv)[16], float (&dl)[16]) {
+    }
+    int row_off[G::kKSteps];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qr = 32 * kb + 8 * g4 + 4 * half;
-        const float4 l4 = *(const float4*)(rows + qr);
-        const float4 d4 = *(const float4*)(rows + kTileRows + qr);
-        lv[4 * g4 + 0] = l4.x; lv[4 * g4 + 1] = l4.y; lv[4 * g4 + 2] = l4.z; lv[4 * g4 + 3] = l4.w;
-        dl[4 * g4 + 0] = d4.x; dl[4 * g4 + 1] = d4.y; dl[4 * g4 + 2] = d4.z; dl[4 * g4 + 3] = d4.w;
+    for (int t = 0; t < G::kKSteps; ++t) row_off[t] = G::at(col, 2 * t + half);
+    const int key = kw0 + col;
+
+    auto step = [&](int jt, auto stage_tag) {
+      constexpr int st = decltype(stage_tag)::value;
+      const bool on = jt < n_qt && active(jt);
+      f32x16 s[2], dp[2];   // the first MFMA of each chain starts from zero
+      // ---- phase 1: S = Q K^T and dP = dO V^T (rows 32 kb + 8(r/4) + 4 half + r%4
+      // of the tile by this lane's key), operands two steps ahead of their MFMAs
+      if (on) {
+        const char* qs = smem_q[st];
+        const char* dos = smem_do[st];
+        __builtin_amdgcn_s_setprio(2);
+        static_for<2>([&](auto kb_tag) {
+          constexpr int kb = decltype(kb_tag)::value;
+          constexpr int kAhead = 2;
+          bf16x8 qa[kAhead + 1], da[kAhead + 1];
+          auto read_rows = [&](int t) {
+            const int off = row_off[t] + kb * 32 * G::kRowBytes;
+            qa[t % (kAhead + 1)] = *(const bf16x8*)(qs + off);
+            da[t % (kAhead + 1)] = *(const bf16x8*)(dos + off);
+          };
+#pragma unroll
+          for (int t = 0; t < kAhead; ++t) read_rows(t);
+#pragma unroll
+          for (int t = 0; t < G::kKSteps; ++t) {
+            if (t + kAhead < G::kKSteps) read_rows(t + kAhead);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t % (kAhead + 1)], kreg[t],
+                                                            t == 0 ? f32x16{} : s[kb], 0, 0, 0);
+            dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t % (kAhead + 1)], vreg[t],
+                                                             t == 0 ? f32x16{} : dp[kb], 0, 0, 0);
+          }
+        });
+        __builtin_amdgcn_s_setprio(0);
       }
-    };
-    // P = exp2(S*c - LSE*log2e), dS = P (dP - D) of block kb; masked keys get
-    // P = 0. Both are rounded to bf16 as the B operands of the transposed
-    // products, 16 queries per MFMA, in the order the forward uses for its P.
-    auto pds = [&](auto kb_tag, const float (&lv)[16], const float (&dl)[16]) {
-      constexpr int kb = decltype(kb_tag)::value;
+      lds_barrier();
+      // ---- phase 2: P = exp2(S c - LSE log2 e), dS = P (dP - D), masked keys
+      // P = 0; both rounded to bf16 in the order the forward uses for its P,
+      // and stored for group B
+      if (on) {
+        const float* rows = smem_rows[st];
+        const int q0 = jt * kTileRows;
+        const bool need_mask = !kCausal ? (q0 + kTileRows > w.sq)
+                                        : ((q0 + kTileRows > w.sq) || kw0 + 31 > q0 + causal_off);
+        bf16x8 pb[4], dsb[4];
+        auto pds = [&](auto mask_tag) {
+          constexpr bool kMask = decltype(mask_tag)::value;
+          static_for<2>([&](auto kb_tag) {
+            constexpr int kb = decltype(kb_tag)::value;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lv[r]));
-        if constexpr (kMask) {
-          const int i = q0 + 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
-          if (i >= w.sq || (kCausal && key > i + causal_off)) pv = 0.f;
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int qr = 32 * kb + 8 * g4 + 4 * half;
+              const float4 l4 = *(const float4*)(rows + qr);
+              const float4 d4 = *(const float4*)(rows + kTileRows + qr);
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+              const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lv[e]));
+                if constexpr (kMask) {
+                  const int i = q0 + qr + e;
+                  if (i >= w.sq || (kCausal && key > i + causal_off)) pv = 0.f;
+                }
+                const float ds = pv * (dp[kb][r] - dl[e]);
+                pb[2 * kb + r / 8][r % 8] = (bf16_t)pv;
+                dsb[2 * kb + r / 8][r % 8] = (bf16_t)ds;
+              }
+            }
+          });
+        };
+        if (need_mask) pds(std::true_type());
+        else pds(std::false_type());
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          *(LDS_AS bf16x8*)(pds_lds + 1024 * k + 16 * ln) = pb[k];
+          *(LDS_AS bf16x8*)(pds_lds + 1024 * (4 + k) + 16 * ln) = dsb[k];
         }
-        const float ds = pv * (dp[kb][r] - dl[r]);
-        pb[2 * kb + r / 8][r % 8] = (bf16_t)pv;
-        dsb[2 * kb + r / 8][r % 8] = (bf16_t)ds;
       }
+      lds_barrier();
     };
-    // dV^T += dO^T P and dK^T += Q^T dS: pair i (16-query step i / kDBlocks,
-    // d block i % kDBlocks) reads the tiles transposed, three pairs ahead
-    constexpr int kN = 4 * G::kDBlocks;
-    constexpr int kAheadT = 3;
-    bf16x8 ad[kAheadT + 1], aq[kAheadT + 1];
-    auto read_t = [&](int i) {
-      const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
-      const int o0 = tl.tr_off[0][db] + 16 * ks16 * G::kRowBytes;
-      const int o1 = tl.tr_off[1][db] + 16 * ks16 * G::kRowBytes;
-      const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o0));
-      const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o1));
-      const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o0));
-      const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o1));
-      ad[i % (kAheadT + 1)] = bf16x8{dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
-      aq[i % (kAheadT + 1)] = bf16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-    };
-    auto dvdk = [&](int i) {
-      if (i + kAheadT < kN) read_t(i + kAheadT);
-      const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
-      dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[i % (kAheadT + 1)], pb[ks16],
-                                                          dvacc[db], 0, 0, 0);
-      dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i % (kAheadT + 1)], dsb[ks16],
-                                                          dkacc[db], 0, 0, 0);
-    };
-
-    float lv[16], dl[16];
-    sdp(std::integral_constant<int, 0>());
-    read_rowvals(0, lv, dl);
-    sdp(std::integral_constant<int, 1>());
-    pds(std::integral_constant<int, 0>(), lv, dl);
-    read_rowvals(1, lv, dl);
-#pragma unroll
-    for (int i = 0; i < kAheadT; ++i) read_t(i);
-#pragma unroll
-    for (int i = 0; i < kN / 2; ++i) dvdk(i);
-    pds(std::integral_constant<int, 1>(), lv, dl);
-#pragma unroll
-    for (int i = kN / 2; i < kN; ++i) dvdk(i);
-
-    // schedule (one stream): block 0's S/dP; its LSE/D reads and block 1's
-    // S/dP with block 0's P/dS arithmetic between the MFMAs; block 1's LSE/D
-    // and the first transposed reads, then the products of 16-query steps 0-1
-    // with block 1's P/dS arithmetic between them; then steps 2-3
-    constexpr int kValu = kMask ? 8 : 5;   // vector instructions per MFMA slot
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int t = 0; t < G::kKSteps; ++t) {
-      if (t + 2 < G::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4, 0);
-#pragma unroll
-    for (int t = 0; t < G::kKSteps; ++t) {
-      if (t + 2 < G::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4 * kAheadT, 0);
-#pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      if (i + kAheadT < kN) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      if (i < kN / 2) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
-    }
-  };
-
-  // Tile loop over a ring of three stages: tile jt lives in stage (jt - t0) % 3.
-  // Step jt waits for its own copies of tile jt (issued two steps earlier; only
-  // those of tile jt+1 may still be outstanding), and one barrier then makes
-  // tile jt visible and shows that every wave has finished step jt-1, so the
-  // copies of tile jt+2 may overwrite the stage tile jt-1 used.
-  auto step = [&](int jt, auto stage_tag) {
-    constexpr int st = decltype(stage_tag)::value;
-    if (jt + 1 < n_qt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kOps));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // the tiles' copies of step t0 (issued by group B) have landed
     lds_barrier();
-    if (jt + 2 < n_qt) copy_tile(jt + 2, std::integral_constant<int, (st + 2) % 3>());
-    // a wave whose first key no query of the tile sees has nothing to add
-    if (!kCausal || jt * kTileRows + kTileRows - 1 + causal_off >= kw0) {
-      // causal: the masked form only on tiles that need it. The non-causal
-      // kernel keeps one form (the masked one, whose extra vector work is
-      // interleaved under the MFMAs): with both, its registers overflow.
-      const int q0 = jt * kTileRows;
-      if (!kCausal || (q0 + kTileRows > w.sq) || kw0 + 31 > q0 + causal_off)
-        compute(jt, stage_tag, std::true_type());
-      else
-        compute(jt, stage_tag, std::false_type());
+    int jt = t0;
+    for (; jt + 3 <= n_qt + 1; jt += 3) {
+      step(jt, std::integral_constant<int, 0>());
+      step(jt + 1, std::integral_constant<int, 1>());
+      step(jt + 2, std::integral_constant<int, 2>());
+    }
+    if (jt <= n_qt) step(jt, std::integral_constant<int, 0>());
+    if (jt + 1 <= n_qt) step(jt + 1, std::integral_constant<int, 1>());
+  };
+
+  auto run_b = [&]() __attribute__((always_inline)) {
+    f32x16 dvacc[G::kDBlocks], dkacc[G::kDBlocks];
+#pragma unroll
+    for (int db = 0; db < G::kDBlocks; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dvacc[db][i] = dkacc[db][i] = 0.f;
+    TileLane<kD> tl;
+    tl.init(lane, sub, stride);
+    const i32x4 q_rsrc = make_buffer_rsrc(
+        (const char*)p.q + (size_t)w.q_start * stride + w.head * G::kRowBytes,
+        (uint32_t)w.sq * stride);
+    const i32x4 do_rsrc = make_buffer_rsrc(
+        (const char*)p.dout + (size_t)w.q_start * stride + w.head * G::kRowBytes,
+        (uint32_t)w.sq * stride);
+    const uint32_t q_lds0 = lds_address(&smem_q[0][1024 * sub]);
+    const uint32_t do_lds0 = lds_address(&smem_do[0][1024 * sub]);
+    const uint32_t rows_lds0 = lds_address(&smem_rows[0][0]);
+    const size_t row_base = (size_t)w.head * p.total_q + w.q_start;
+    // a tile's copies: Q and dO rows, then LSE*log2e and D of its 64 rows (every
+    // wave of the group fetches the same 512 bytes)
+    auto copy_tile = [&](int jt, auto stage_tag) {
+      constexpr int st = decltype(stage_tag)::value;
+      tl.template copy<st * G::kTileBytes>(q_lds0, q_rsrc, jt * kTileRows, stride);
+      tl.template copy<st * G::kTileBytes>(do_lds0, do_rsrc, jt * kTileRows, stride);
+      const size_t r = row_base + min(jt * kTileRows + lane, w.sq - 1);
+      const uint32_t rl = __builtin_amdgcn_readfirstlane(rows_lds0 + st * 2 * kTileRows * 4);
+      lds_dma_global_4(rl, p.lse2 + r);
+      lds_dma_global_4(rl + kTileRows * 4, p.delta + r);
+    };
+
+    // step s: stage st holds tile s, (st + 2) % 3 tile s-1, (st + 1) % 3 receives s+1
+    auto step = [&](int jt, auto stage_tag) {
+      constexpr int st = decltype(stage_tag)::value;
+      const bool on = jt - 1 >= t0 && active(jt - 1);
+      // ---- phase 1: copies of tile jt+1, P/dS of tile jt-1
+      if (jt + 1 < n_qt) copy_tile(jt + 1, std::integral_constant<int, (st + 1) % 3>());
+      bf16x8 pb[4], dsb[4];
+      if (on) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          pb[k] = *(const LDS_AS bf16x8*)(pds_lds + 1024 * k + 16 * ln);
+          dsb[k] = *(const LDS_AS bf16x8*)(pds_lds + 1024 * (4 + k) + 16 * ln);
+        }
+      }
+      lds_barrier();
+      // ---- phase 2: dV^T += dO^T P and dK^T += Q^T dS of tile jt-1: pair i
+      // (16-query step i / kDBlocks, d block i % kDBlocks) reads the tiles
+      // transposed, three pairs ahead
+      if (on) {
+        const char* qs = smem_q[(st + 2) % 3];
+        const char* dos = smem_do[(st + 2) % 3];
+        constexpr int kN = 4 * G::kDBlocks;
+        constexpr int kAheadT = 3;
+        bf16x8 ad[kAheadT + 1], aq[kAheadT + 1];
+        auto read_t = [&](int i) {
+          const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
+          const int o0 = tl.tr_off[0][db] + 16 * ks16 * G::kRowBytes;
+          const int o1 = tl.tr_off[1][db] + 16 * ks16 * G::kRowBytes;
+          const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o0));
+          const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(dos + o1));
+          const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o0));
+          const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(qs + o1));
+          ad[i % (kAheadT + 1)] =
+              bf16x8{dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
+          aq[i % (kAheadT + 1)] =
+              bf16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+        };
+        __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+        for (int i = 0; i < kAheadT; ++i) read_t(i);
+#pragma unroll
+        for (int i = 0; i < kN; ++i) {
+          if (i + kAheadT < kN) read_t(i + kAheadT);
+          const int ks16 = i / G::kDBlocks, db = i % G::kDBlocks;
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[i % (kAheadT + 1)], pb[ks16],
+                                                              dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i % (kAheadT + 1)], dsb[ks16],
+                                                              dkacc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      // the copies of tile jt+1 have landed before the barrier that publishes them
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      lds_barrier();
+    };
+    if (t0 < n_qt) copy_tile(t0, std::integral_constant<int, 0>());
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    int jt = t0;
+    for (; jt + 3 <= n_qt + 1; jt += 3) {
+      step(jt, std::integral_constant<int, 0>());
+      step(jt + 1, std::integral_constant<int, 1>());
+      step(jt + 2, std::integral_constant<int, 2>());
+    }
+    if (jt <= n_qt) step(jt, std::integral_constant<int, 0>());
+    if (jt + 1 <= n_qt) step(jt + 1, std::integral_constant<int, 1>());
+
+    // dV = sum P^T dO, dK = tau sum dS^T Q for this lane's key
+    const int key = kw0 + col;
+    if (key < w.sk) {
+      const size_t off = (size_t)(w.k_start + key) * p.heads * kD + (size_t)w.head * kD;
+      store_bf16_rows((bf16_t*)p.dv + off, dvacc, G::kDBlocks, 1.f, half);
+      store_bf16_rows((bf16_t*)p.dk + off, dkacc, G::kDBlocks, p.scale, half);
     }
   };
-  if (t0 < n_qt) copy_tile(t0, std::integral_constant<int, 0>());
-  if (t0 + 1 < n_qt) copy_tile(t0 + 1, std::integral_constant<int, 1>());
-  int jt = t0;
-  for (; jt + 3 <= n_qt; jt += 3) {
-    step(jt, std::integral_constant<int, 0>());
-    step(jt + 1, std::integral_constant<int, 1>());
-    step(jt + 2, std::integral_constant<int, 2>());
-  }
-  if (jt < n_qt) step(jt, std::integral_constant<int, 0>());
-  if (jt + 1 < n_qt) step(jt + 1, std::integral_constant<int, 1>());
 
-  // dV = sum P^T dO, dK = tau sum dS^T Q for this lane's key
-  const int key = kw0 + col;
-  if (key < w.sk) {
-    const size_t off = (size_t)(w.k_start + key) * p.heads * kD + (size_t)w.head * kD;
-    store_bf16_rows((bf16_t*)p.dv + off, dvacc, G::kDBlocks, 1.f, half);
-    store_bf16_rows((bf16_t*)p.dk + off, dkacc, G::kDBlocks, p.scale, half);
-  }
+  if (grp == 0) run_a();
+  else run_b();
 }
 
 // ---------------------------------------------------------------- dQ
@@ -647,7 +664,7 @@ hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t stream) {
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   if (items > 0)
     hipLaunchKernelGGL((fmha_bwd_dkdv_kernel<kD, kCausal>), dim3((unsigned)items),
-                       dim3(kBwdWaves * 64), 0, stream, p);
+                       dim3(2 * kBwdWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
