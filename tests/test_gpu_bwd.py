@@ -148,7 +148,25 @@ def test_bwd_c2_dense_2225_two_heads():
     assert all(np.isfinite(g).all() for g in got)
 
 
-@pytest.mark.parametrize("name", ["c3_varlen_causal_8k", "c4_varlen_causal_32k"])
+@pytest.mark.timeout(600)
+def test_bwd_c3_full():
+    """c3 at full size with the benchmark step's dO = 2 O / n (n = numel(O), O the
+    oracle's forward output), every gradient element of every document and head
+    against the oracle (about half a minute of fp64 on the host's cores)."""
+    w = WORKLOADS["c3_varlen_causal_8k"]
+    inp = workload_inputs(w)
+    n = w.total_q * w.heads * w.head_dim
+    o_ref, _ = oracle.attention(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, w.causal,
+                                w.softmax_scale)
+    dout = torch.from_numpy(2.0 * o_ref / n).float().to(torch.bfloat16)
+    got = _gpu_bwd(inp, dout, w.causal, w.softmax_scale)
+    print("c3 backward: oracle on every row", flush=True)
+    ref, t = oracle.attention_backward(inp.q, inp.k, inp.v, dout, inp.cu_q, inp.cu_k, w.causal,
+                                       w.softmax_scale, rounding_scale=True)
+    _check(got, ref, t, f"{w.name} full")
+
+
+@pytest.mark.parametrize("name", ["c4_varlen_causal_32k"])
 def test_bwd_varlen_causal_full_size_sampled(name):
     """The varlen causal step's shapes at full size, with dO on the scale of the
     benchmark loss's gradient 2 O / n (n = numel(O)): exactly 2 O / n from the
