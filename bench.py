@@ -444,42 +444,64 @@ def visible_scores(w):
 
 
 def summarize_sq(csv_path, w, simds=1024, xcds=8):
-    """Per-launch averages of the counters of a rocprofv3 --pmc --counters run
-    for the FMHA kernel, and three checks against the workload:
-    MFMA FLOP = 512 x the MFMA MOPS counters, against the counted FLOP (the
-    kernel also multiplies the masked part of its diagonal tiles);
+    """Per-launch averages of the counters of a rocprofv3 --pmc --counters run,
+    kernel by kernel (the forward's one kernel, or the backward's dQ and dK/dV
+    kernels), and the checks the counters present allow:
+    MFMA FLOP = 512 x the MFMA MOPS counters, against the counted forward FLOP
+    (the kernel also multiplies the masked part of its diagonal tiles);
     transcendental instructions x 64 lanes per visible score (one exp2 per
     score, plus the rescale exp2s and the epilogue's log);
     MFMA busy cycles per SIMD over the elapsed cycles per XCD (GRBM_GUI_ACTIVE
-    sums the XCDs)."""
+    sums the XCDs);
+    LDS bank- and address-conflict stall cycles over the cycles the LDS spends
+    on indexed (ds_read/ds_write) work, and per LDS instruction."""
     per = {}
     for r in _counter_rows(csv_path):
-        if "fmha_fwd" not in r["Kernel_Name"]:
+        name = r["Kernel_Name"]
+        if "fmha_fwd" not in name and "fmha_bwd" not in name:
             continue
-        key = (r["Dispatch_Id"], r["Kernel_Name"])
-        d = per.setdefault(key, {})
+        d = per.setdefault(name, {}).setdefault(r["Dispatch_Id"], {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     if not per:
         raise SystemExit(f"{csv_path}: no FMHA dispatches")
-    names = sorted({k[1] for k in per})
-    counters = sorted({c for d in per.values() for c in d})
-    avg = {c: sum(d.get(c, 0.0) for d in per.values()) / len(per) for c in counters}
-    lines = [f"{len(per)} dispatches of {', '.join(names)}"]
-    for c in counters:
-        lines.append(f"  {c:32s} {avg[c]:.4e}")
-    mops = sum(v for c, v in avg.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
-    if mops:
-        lines.append(f"  MFMA FLOP (512 x MOPS)           {512 * mops:.4e}  "
-                     f"= {512 * mops / w.flops():.4f} x the counted {w.flops():.4e}")
-    if "SQ_INSTS_VALU_TRANS_F32" in avg:
-        vis = visible_scores(w)
-        lines.append(f"  transcendental lane ops / visible score  "
-                     f"{64 * avg['SQ_INSTS_VALU_TRANS_F32'] / vis:.4f}  ({vis:.4e} visible scores)")
-    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
-        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
-        elapsed = avg["GRBM_GUI_ACTIVE"] / xcds
-        lines.append(f"  MFMA busy per SIMD / elapsed     {busy:.4e} / {elapsed:.4e} = "
-                     f"{busy / elapsed:.3f}")
+    lines = []
+    for name in sorted(per):
+        disp = per[name]
+        counters = sorted({c for d in disp.values() for c in d})
+        avg = {c: sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in counters}
+        if lines:
+            lines.append("")
+        lines.append(f"{len(disp)} dispatches of {name}")
+        for c in counters:
+            lines.append(f"  {c:32s} {avg[c]:.4e}")
+        fwd = "fmha_fwd" in name
+        mops = sum(v for c, v in avg.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+        if mops and fwd:
+            lines.append(f"  MFMA FLOP (512 x MOPS)           {512 * mops:.4e}  "
+                         f"= {512 * mops / w.flops():.4f} x the counted {w.flops():.4e}")
+        elif mops:
+            lines.append(f"  MFMA FLOP (512 x MOPS)           {512 * mops:.4e}  "
+                         f"= {512 * mops / w.flops():.4f} x the counted forward {w.flops():.4e}")
+        if "SQ_INSTS_VALU_TRANS_F32" in avg and fwd:
+            vis = visible_scores(w)
+            lines.append(f"  transcendental lane ops / visible score  "
+                         f"{64 * avg['SQ_INSTS_VALU_TRANS_F32'] / vis:.4f}  "
+                         f"({vis:.4e} visible scores)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+            busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+            elapsed = avg["GRBM_GUI_ACTIVE"] / xcds
+            lines.append(f"  MFMA busy per SIMD / elapsed     {busy:.4e} / {elapsed:.4e} = "
+                         f"{busy / elapsed:.3f}")
+        for c, what in (("SQ_LDS_BANK_CONFLICT", "bank-conflict"),
+                        ("SQ_LDS_ADDR_CONFLICT", "address-conflict")):
+            if c not in avg:
+                continue
+            if avg.get("SQ_LDS_IDX_ACTIVE"):
+                lines.append(f"  LDS {what} cycles / indexed LDS cycles  "
+                             f"{avg[c] / avg['SQ_LDS_IDX_ACTIVE']:.4f}")
+            if avg.get("SQ_INSTS_LDS"):
+                lines.append(f"  LDS {what} cycles / LDS instruction     "
+                             f"{avg[c] / avg['SQ_INSTS_LDS']:.4f}")
     return "\n".join(lines)
 
 

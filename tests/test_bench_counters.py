@@ -65,3 +65,31 @@ def test_summarize_sq_sums_xcds_and_averages_dispatches(tmp_path):
     elapsed = 2.0 * 8 * 4096 / 8
     assert f"{busy / elapsed:.3f}" in text
     assert "999999" not in text and "copyBuffer" not in text
+
+
+def test_summarize_sq_splits_backward_kernels_and_reports_lds_conflicts(tmp_path):
+    b = _bench()
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    dq = "void fmha::fmha_bwd_dq_kernel<128, true>(fmha::BwdParams)"
+    dkdv = "void fmha::fmha_bwd_dkdv_kernel<128, true>(fmha::BwdParams)"
+    for disp, kern, conflict in ((1, dq, 5.0), (2, dkdv, 0.0), (3, dq, 15.0), (4, dkdv, 0.0)):
+        for xcd in range(8):
+            rows.append(f'{disp},"{kern}",SQ_LDS_BANK_CONFLICT,{conflict}')
+            rows.append(f'{disp},"{kern}",SQ_LDS_IDX_ACTIVE,1000')
+            rows.append(f'{disp},"{kern}",SQ_INSTS_LDS,50')
+            rows.append(f'{disp},"{kern}",SQ_INSTS_VALU_TRANS_F32,7')
+    p = tmp_path / "c.csv"
+    p.write_text("\n".join(rows) + "\n")
+    w = Workload("t", "t", heads=1, head_dim=128, causal=True, doc_lens=((8, 8),))
+    text = b.summarize_sq(str(p), w)
+    blocks = text.split("\n\n")
+    assert len(blocks) == 2
+    by_kernel = {blk.splitlines()[0]: blk for blk in blocks}
+    assert set(by_kernel) == {f"2 dispatches of {dq}", f"2 dispatches of {dkdv}"}
+    q = by_kernel[f"2 dispatches of {dq}"]
+    # mean over the two dQ dispatches of the 8-XCD sums: conflicts 80, indexed cycles 8000
+    assert "bank-conflict cycles / indexed LDS cycles  0.0100" in q
+    assert "bank-conflict cycles / LDS instruction     0.2000" in q
+    assert "bank-conflict cycles / indexed LDS cycles  0.0000" in by_kernel[f"2 dispatches of {dkdv}"]
+    # the visible-score check belongs to the forward kernels only
+    assert "visible score" not in text
