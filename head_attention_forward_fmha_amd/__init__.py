@@ -130,7 +130,8 @@ def fwd(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[in
 
     q [total_q, h, d] / k, v [total_k, h, d] with cu_seqlens (int32 [batch+1]),
     or dense q [b, sq, h, d] / k, v [b, sk, h, d]. d must be 64 or 128.
-    variant: "auto", "four_wave" or "pingpong" (kernel choice; same function).
+    variant: "auto", "four_wave", "pingpong", "pipelined" or "wide" (kernel
+    choice; same function).
     """
     import torch
     lib = _lib.load()
@@ -254,7 +255,7 @@ def fwd_splitkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None,
         raise ValueError("k and v must match, with q's heads and head_dim")
     if num_splits == "auto":
         n_split = splitkv_num_splits(s["batch"], s["max_q"], s["max_k"], s["heads"], causal,
-                                     variant if variant != "pipelined" else "auto")
+                                     variant if variant not in ("pipelined", "wide") else "auto")
     else:
         n_split = int(num_splits)
     scale = 1.0 / math.sqrt(s["d"]) if softmax_scale is None else float(softmax_scale)

@@ -19,7 +19,7 @@ FMHA_ERR_UNSUPPORTED = 2
 FMHA_ERR_LAUNCH = 3
 NOALLOC_SCRATCH_BYTES = 16 << 20      # FMHA_NOALLOC_SCRATCH_BYTES of include/fmha.h
 
-VARIANTS = {"auto": 0, "four_wave": 1, "pingpong": 2, "pipelined": 3}
+VARIANTS = {"auto": 0, "four_wave": 1, "pingpong": 2, "pipelined": 3, "wide": 4}
 
 EXPORTED_SYMBOLS = (
     "fmha_fwd",

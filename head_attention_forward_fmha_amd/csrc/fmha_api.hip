@@ -131,7 +131,7 @@ fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,
                                   max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
                                   softmax_scale, out, lse);
   if (st != FMHA_OK) return st;
-  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PIPELINED) return FMHA_ERR_INVALID_ARG;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_WIDE) return FMHA_ERR_INVALID_ARG;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
   fmha::FwdParams p = make_params(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
                                   max_seqlen_q, max_seqlen_k, num_heads, softmax_scale, out, lse);
@@ -164,8 +164,8 @@ fmha_status_t fmha_fwd_fp8pv_variant(const void* q, const void* k, const uint8_t
                                   causal, softmax_scale, out, lse);
   if (st != FMHA_OK) return st;
   if (head_dim != 128) return FMHA_ERR_UNSUPPORTED;
-  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PIPELINED) return FMHA_ERR_INVALID_ARG;
-  if (variant == FMHA_VARIANT_PIPELINED) return FMHA_ERR_UNSUPPORTED;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_WIDE) return FMHA_ERR_INVALID_ARG;
+  if (variant == FMHA_VARIANT_PIPELINED || variant == FMHA_VARIANT_WIDE) return FMHA_ERR_UNSUPPORTED;
   if (total_k > 0 && v_scale == nullptr) return FMHA_ERR_INVALID_ARG;
   if (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 3u)) return FMHA_ERR_INVALID_ARG;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
@@ -204,8 +204,8 @@ fmha_status_t fmha_fwd_fp4pv_variant(const void* q, const void* k, const uint8_t
                                   causal, softmax_scale, out, lse);
   if (st != FMHA_OK) return st;
   if (head_dim != 128) return FMHA_ERR_UNSUPPORTED;
-  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PIPELINED) return FMHA_ERR_INVALID_ARG;
-  if (variant == FMHA_VARIANT_PIPELINED) return FMHA_ERR_UNSUPPORTED;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_WIDE) return FMHA_ERR_INVALID_ARG;
+  if (variant == FMHA_VARIANT_PIPELINED || variant == FMHA_VARIANT_WIDE) return FMHA_ERR_UNSUPPORTED;
   if (total_k > 0 && v_mx_scale == nullptr) return FMHA_ERR_INVALID_ARG;
   if (v_mx_scale && (reinterpret_cast<uintptr_t>(v_mx_scale) & 3u)) return FMHA_ERR_INVALID_ARG;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
@@ -262,8 +262,8 @@ fmha_status_t fmha_fwd_splitkv(const void* q, const void* k, const void* v,
                                   max_seqlen_q, max_seqlen_k, num_heads, head_dim, causal,
                                   softmax_scale, out, lse);
   if (st != FMHA_OK) return st;
-  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_PIPELINED) return FMHA_ERR_INVALID_ARG;
-  if (variant == FMHA_VARIANT_PIPELINED) return FMHA_ERR_UNSUPPORTED;
+  if (variant < FMHA_VARIANT_AUTO || variant > FMHA_VARIANT_WIDE) return FMHA_ERR_INVALID_ARG;
+  if (variant == FMHA_VARIANT_PIPELINED || variant == FMHA_VARIANT_WIDE) return FMHA_ERR_UNSUPPORTED;
   if (num_splits < 1 || num_splits > fmha::kMaxSplits) return FMHA_ERR_INVALID_ARG;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FMHA_OK;
   fmha::FwdParams p = make_params(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,

@@ -2,7 +2,8 @@
 //
 // The per-wave tile math (Q in registers, S^T = K Q^T and O^T += V^T P^T on
 // 32x32 MFMA, exp2-domain online softmax) lives in fmha_device.h. This file
-// arranges waves, LDS stages and barriers around it in two ways:
+// arranges waves, LDS stages and barriers around it in four ways; the first
+// two are the ones the automatic choice takes:
 //
 //  * fmha_fwd_kernel: 4 waves (128 query rows) per workgroup, two workgroups
 //    per CU. Each wave runs copy-wait / Q.K^T / softmax / P.V per tile; the
@@ -19,9 +20,17 @@
 //    tiles are shared by 256 query rows (half the LDS and L2 traffic per
 //    FLOP of the 4-wave kernel).
 //
+//  * fmha_fwd_pipe_kernel: 4 waves of 32 rows, each software-pipelined over
+//    half-tiles of 32 keys (its own MFMAs in flight under its own softmax).
+//
+//  * fmha_fwd_wide_kernel: 4 waves of 64 rows, one per SIMD, each K and V
+//    operand read from LDS feeding two MFMAs, Q and O in the accumulation
+//    registers; the same per-wave software pipeline.
+//
 // Causal launches are persistent (each workgroup walks its XCD's share of the
-// work items, see for_each_item); every kernel streams K/V tiles of 64 keys through a double buffer
-// with buffer_load ... lds copies ordered by explicit vmcnt waits and barriers.
+// work items, see for_each_item); every kernel streams K/V tiles of 64 keys
+// through a ring of two or three LDS stages with buffer_load ... lds copies,
+// ordered by explicit vmcnt waits and barriers.
 
 #include <algorithm>
 #include <atomic>
@@ -555,6 +564,413 @@ void fmha_fwd_pipe_kernel(FwdParams params) {
   for_each_item<kCausal, false>(params, run_item);
 }
 
+// ---------------------------------------------------------------- 64-row-wave kernel
+
+// 4 waves (256 query rows) per workgroup, one workgroup per CU, one wave per
+// SIMD with up to 512 registers. Each wave owns two 32-row blocks of the work
+// item, blocks w and 7 - w (so that under a causal mask every wave has the
+// same work), and gives every K and V operand it reads from LDS to two MFMAs,
+// one per block: half the LDS bytes per MFMA of the 32-row kernels. The wave
+// software-pipelines its work over half-tiles of 32 keys as the pipelined
+// kernel does: step u runs the softmax of half-tile u (vector ALU), S of
+// half-tile u+1 (Q.K^T MFMAs, then) and O += P V of half-tile u-1 (P.V MFMAs).
+//
+// Register files. Q (the B operand of S^T = K Q^T) and O^T (the accumulator
+// of O^T += V^T P^T) live in the accumulation registers (AGPRs), S^T and P in
+// the vector registers (VGPRs). The MFMAs are inline asm so that each operand
+// is read from and written to the file it lives in, without copies between
+// the files. The compiler therefore does not see them: the wait states the
+// ISA requires between an MFMA and a later instruction that reads or
+// overwrites its result (at most 19 for these 8-pass MFMAs), or between a
+// vector write of an operand and the MFMA that reads it, come from the
+// schedule (in a steady step, the 16 P.V MFMAs issued after the last Q.K^T
+// MFMA of a half-tile keep its S from being read before the next step) or
+// from mfma_settle where the schedule does not provide them.
+constexpr int kWavesWide = 4;
+constexpr int kBMWide = kWavesWide * 64;  // query rows per workgroup
+static_assert(kBMWide == kRowsWide, "64-row-wave block height");
+constexpr int kStagesWide = 3;            // K/V ring depth
+typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
+
+// S^T = K Q^T (first d step: zero accumulator) and S^T += K Q^T
+__device__ __forceinline__ void mfma_s_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma_s(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "a"(q));
+}
+// O^T += V^T P^T, O^T in AGPRs
+__device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& v, const bf16x8& p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+}
+
+// 24 wait states after the asm MFMAs issued so far, ordered (through the
+// operands, which the statement claims to read and write) before every later
+// access of the named registers by the compiler's own instructions.
+#define FMHA_MFMA_SETTLE "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+
+template <class WT>
+__device__ __forceinline__ void mfma_settle_o(WT& a, WT& b) {
+  static_assert(WT::kDBlocks == 4 || WT::kDBlocks == 2, "head_dim 128 or 64");
+  if constexpr (WT::kDBlocks == 4)
+    asm volatile(FMHA_MFMA_SETTLE
+                 : "+a"(a.oacc[0]), "+a"(a.oacc[1]), "+a"(a.oacc[2]), "+a"(a.oacc[3]),
+                   "+a"(b.oacc[0]), "+a"(b.oacc[1]), "+a"(b.oacc[2]), "+a"(b.oacc[3]));
+  else
+    asm volatile(FMHA_MFMA_SETTLE
+                 : "+a"(a.oacc[0]), "+a"(a.oacc[1]), "+a"(b.oacc[0]), "+a"(b.oacc[1]));
+}
+template <class WT>
+__device__ __forceinline__ void mfma_settle_s(WT& a, WT& b, int set) {
+  if (set == 0) asm volatile(FMHA_MFMA_SETTLE : "+v"(a.hs[0]), "+v"(b.hs[0]));
+  else asm volatile(FMHA_MFMA_SETTLE : "+v"(a.hs[1]), "+v"(b.hs[1]));
+}
+// Q (written by the compiler's loads and moves) before the first Q.K^T MFMA of
+// an item, and the zeroed O before its first P.V MFMA
+template <class WT>
+__device__ __forceinline__ void mfma_settle_q(WT& a, WT& b) {
+  static_assert(WT::kKSteps == 8 || WT::kKSteps == 4, "head_dim 128 or 64");
+  if constexpr (WT::kKSteps == 8) {
+    asm volatile(FMHA_MFMA_SETTLE
+                 : "+a"(a.qreg[0]), "+a"(a.qreg[1]), "+a"(a.qreg[2]), "+a"(a.qreg[3]),
+                   "+a"(a.qreg[4]), "+a"(a.qreg[5]), "+a"(a.qreg[6]), "+a"(a.qreg[7]));
+    asm volatile(FMHA_MFMA_SETTLE
+                 : "+a"(b.qreg[0]), "+a"(b.qreg[1]), "+a"(b.qreg[2]), "+a"(b.qreg[3]),
+                   "+a"(b.qreg[4]), "+a"(b.qreg[5]), "+a"(b.qreg[6]), "+a"(b.qreg[7]));
+  } else {
+    asm volatile(FMHA_MFMA_SETTLE
+                 : "+a"(a.qreg[0]), "+a"(a.qreg[1]), "+a"(a.qreg[2]), "+a"(a.qreg[3]),
+                   "+a"(b.qreg[0]), "+a"(b.qreg[1]), "+a"(b.qreg[2]), "+a"(b.qreg[3]));
+  }
+  mfma_settle_o(a, b);
+}
+
+// S^T of half kH of the K tile at ks into hs[kH] of both blocks: one K operand
+// read per d step, two MFMAs on it. Reads run two steps ahead.
+template <int kH, class WT>
+__device__ __forceinline__ void wide_qk(WT& a, WT& b, const char* ks) {
+  constexpr int kN = WT::kKSteps;
+  bf16x8 ka[3];
+  auto rk = [&](int t) {
+    ka[t % 3] = *(const bf16x8*)(ks + a.k_off[t] + kH * 32 * WT::kRowBytes);
+  };
+  rk(0);
+  rk(1);
+#pragma unroll
+  for (int t = 0; t < kN; ++t) {
+    if (t + 2 < kN) rk(t + 2);
+    if (t == 0) {
+      mfma_s_first(a.hs[kH], ka[0], a.qreg[0]);
+      mfma_s_first(b.hs[kH], ka[0], b.qreg[0]);
+    } else {
+      mfma_s(a.hs[kH], ka[t % 3], a.qreg[t]);
+      mfma_s(b.hs[kH], ka[t % 3], b.qreg[t]);
+    }
+  }
+}
+
+// O^T += V^T P^T of half kH of the V tile at vs for both blocks (P in hp[kH]):
+// one transposed V operand read per (16-key step, d block), two MFMAs on it.
+template <int kH, class WT>
+__device__ __forceinline__ void wide_pv(WT& a, WT& b, const char* vs) {
+  constexpr int kN = WT::kHalfPv;
+  bf16x8 va[3];
+  va[0] = a.template read_v_half<kH>(vs, 0);
+  va[1] = a.template read_v_half<kH>(vs, 1);
+#pragma unroll
+  for (int t = 0; t < kN; ++t) {
+    if (t + 2 < kN) va[(t + 2) % 3] = a.template read_v_half<kH>(vs, t + 2);
+    mfma_o(a.oacc[t % WT::kDBlocks], va[t % 3], a.hp[kH][t / WT::kDBlocks]);
+    mfma_o(b.oacc[t % WT::kDBlocks], va[t % 3], b.hp[kH][t / WT::kDBlocks]);
+  }
+}
+
+// A pending rescale of O (alpha_o != 1 in a lane of either block), after every
+// P.V MFMA issued so far.
+template <class WT>
+__device__ __forceinline__ void wide_settle_o(WT& a, WT& b) {
+  if (__builtin_amdgcn_ballot_w64(a.alpha_o != 1.f || b.alpha_o != 1.f) != 0) {
+    mfma_settle_o(a, b);
+#pragma unroll
+    for (int db = 0; db < WT::kDBlocks; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        a.oacc[db][i] *= a.alpha_o;
+        b.oacc[db][i] *= b.alpha_o;
+      }
+    mfma_settle_o(a, b);
+    a.alpha_o = 1.f;
+    b.alpha_o = 1.f;
+  }
+}
+
+// The softmax arithmetic of one block's 16 scores of a half-tile, cut into
+// three stages that a steady step spreads over its MFMAs: stage 0 of score i
+// is the folded FMA, stage 1 its exp2, stage 2 the partial sum and, with an
+// odd i, the bf16 pack of scores (i-1, i). Slot k runs stage 0 of score k+1,
+// stage 1 of score k and stage 2 of score k-1, three independent instructions
+// whose inputs were produced a slot (an MFMA) earlier: with one wave per SIMD
+// no other wave hides the latency of a dependent chain. The empty asm
+// statements keep each result at its slot: left alone, the compiler sinks the
+// arithmetic of a block whose results are first used after a branch to behind
+// that branch, out of the MFMA stream.
+template <int kPar, class WT>
+struct ScoreChain {
+  WT& t;
+  float c, nm;
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+  float x[16];
+  float e[16];
+  __device__ __forceinline__ ScoreChain(WT& tile, float c_) : t(tile), c(c_) {
+    nm = (t.m_run == -__builtin_inff()) ? 0.f : -t.m_run * c;
+  }
+  __device__ __forceinline__ void fma(int i) {
+    x[i] = __builtin_fmaf(t.hs[kPar][i], c, nm);
+    asm volatile("" : "+v"(x[i]));
+  }
+  __device__ __forceinline__ void exp(int i) {
+    e[i] = __builtin_amdgcn_exp2f(x[i]);
+    asm volatile("" : "+v"(e[i]));
+  }
+  __device__ __forceinline__ void sum(int i) {
+    rs[i & 3] = (i < 4) ? e[i] : rs[i & 3] + e[i];
+    asm volatile("" : "+v"(rs[i & 3]));
+    if (i & 1) {
+      bf16x2 pr = {(bf16_t)e[i - 1], (bf16_t)e[i]};
+      asm volatile("" : "+v"(pr));
+      t.hp[kPar][i / 8][(i % 8) - 1] = pr[0];
+      t.hp[kPar][i / 8][i % 8] = pr[1];
+    }
+  }
+  // slot k of 16 (k = -1: the stage 0 of score 0 before the first slot; k = 16,
+  // 17: what remains after the last one)
+  __device__ __forceinline__ void slot(int k) {
+    if (k + 1 >= 0 && k + 1 < 16) fma(k + 1);
+    if (k >= 0 && k < 16) exp(k);
+    if (k - 1 >= 0 && k - 1 < 16) sum(k - 1);
+  }
+  __device__ __forceinline__ float total() const { return (rs[0] + rs[1]) + (rs[2] + rs[3]); }
+};
+
+// Steady step u (kPar = u & 1): Q.K^T of half-tile u+1 (half kPar^1 of the K
+// tile at ks), then P.V of half-tile u-1 (half kPar^1 of the V tile at vs),
+// with the softmax of half-tile u spread over both (ScoreChain), the same
+// number of slots of one block after each MFMA of that block. Returns the two
+// blocks' partial row sums of half-tile u.
+template <int kPar, class WT>
+__device__ __forceinline__ float2 wide_step(WT& a, WT& b, const char* ks, const char* vs) {
+  constexpr int kH = kPar ^ 1;
+  constexpr int kN = WT::kKSteps;
+  static_assert(WT::kHalfPv == kN, "Q.K^T and P.V steps pair up one to one");
+  constexpr int kR = 8 / kN;   // slots of a block per MFMA of that block
+  ScoreChain<kPar, WT> sa(a, a.c), sb(b, b.c);
+  auto slots = [&](ScoreChain<kPar, WT>& sc, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = k0; k < k0 + kR; ++k) sc.slot(k);
+  };
+  bf16x8 ka[3], va[3];
+  auto rk = [&](int t) {
+    ka[t % 3] = *(const bf16x8*)(ks + a.k_off[t] + kH * 32 * WT::kRowBytes);
+  };
+  auto rv = [&](int t) { va[t % 3] = a.template read_v_half<kH>(vs, t); };
+  rk(0);
+  rk(1);
+  sa.slot(-1);
+  sb.slot(-1);
+#pragma unroll
+  for (int t = 0; t < kN; ++t) {
+    if (t + 2 < kN) rk(t + 2);
+    if (t == kN - 2) rv(0);
+    if (t == kN - 1) rv(1);
+    if (t == 0) mfma_s_first(a.hs[kH], ka[0], a.qreg[0]);
+    else mfma_s(a.hs[kH], ka[t % 3], a.qreg[t]);
+    slots(sa, kR * t);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t == 0) mfma_s_first(b.hs[kH], ka[0], b.qreg[0]);
+    else mfma_s(b.hs[kH], ka[t % 3], b.qreg[t]);
+    slots(sb, kR * t);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int t = 0; t < kN; ++t) {
+    if (t + 2 < kN) rv(t + 2);
+    mfma_o(a.oacc[t % WT::kDBlocks], va[t % 3], a.hp[kH][t / WT::kDBlocks]);
+    slots(sa, 8 + kR * t);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_o(b.oacc[t % WT::kDBlocks], va[t % 3], b.hp[kH][t / WT::kDBlocks]);
+    slots(sb, 8 + kR * t);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sa.slot(16);
+  sb.slot(16);
+  sa.slot(17);
+  sb.slot(17);
+  return make_float2(sa.total(), sb.total());
+}
+
+template <int kD, bool kCausal>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWavesWide * 64, kWavesWide * 64),
+                          amdgpu_waves_per_eu(1, 1)))
+void fmha_fwd_wide_kernel(FwdParams params) {
+  using WT = WaveTile<kD, kCausal, kPvBf16, kWavesWide>;
+  // d = 128 stores O through a private 4 KB LDS block per wave (epilogue_lds)
+  constexpr bool kStageO = kD == 128;
+  __shared__ __attribute__((aligned(1024))) char smem_k[kStagesWide][WT::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_v[kStagesWide][WT::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_o[kStageO ? kWavesWide * 4096 : 1024];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t k_lds0 = lds_address(&smem_k[0][1024 * wave]);
+  const uint32_t v_lds0 = lds_address(&smem_v[0][1024 * wave]);
+
+  auto run_item = [&](const FwdParams& p, int item) __attribute__((always_inline)) {
+  const WorkItem w = decode_work_item(p, kBMWide, item);
+  if (w.m0 >= w.sq) return;  // uniform over the workgroup
+  const int causal_off = w.sk - w.sq;
+  int kend = w.sk;
+  if (kCausal) kend = min(w.sk, max(0, w.m0 + kBMWide + causal_off));
+  const int n_half = (kend + 31) / 32;
+  const int n_tiles = (kend + kBN - 1) / kBN;
+
+  // block a: rows 32*wave .. +31 of the item (this wave's copies too), block b:
+  // rows 32*(7 - wave) .. +31
+  WT ta, tb;
+  ta.init(p, w, wave, wave);
+  ta.pin_copy_state();
+  tb.init_lanes(p);
+  tb.begin_rows(w, 2 * kWavesWide - 1 - wave);
+  tb.load_q(p, w, tb.qi);
+  ta.alpha_o = 1.f;
+  tb.alpha_o = 1.f;
+  // lane-half tests are formed per item, not hoisted out of the item loop into
+  // scalar registers held across it
+  asm volatile("" : "+v"(ta.half), "+v"(tb.half));
+
+  // the copies of iteration i: K tile i+2 and V tile i+1 (stages (i+2) % 3 and
+  // (i+1) % 3, read last in iteration i-1); they land before iteration i+1 ends.
+  // Returns the number of copy instructions issued.
+  auto copies_rt = [&](int i) __attribute__((always_inline)) -> int {
+    int ops = 0;
+    if (i + 2 < n_tiles) {
+      ta.template copy_k<0>(i + 2, __builtin_amdgcn_readfirstlane(
+                                       k_lds0 + (uint32_t)((i + 2) % kStagesWide) * WT::kTileBytes));
+      ops += WT::kLoadsPerWave;
+    }
+    if (i + 1 < n_tiles) {
+      ta.template copy_v<0>(i + 1, __builtin_amdgcn_readfirstlane(
+                                       v_lds0 + (uint32_t)((i + 1) % kStagesWide) * WT::kVTileBytes));
+      ops += WT::kVLoadsPerWave;
+    }
+    return ops;
+  };
+  // end of an iteration: this wave's copies from the previous one have landed,
+  // then every wave's (and every wave's reads of this iteration are done)
+  auto finish_iteration = [&](bool k_copy, bool v_copy) __attribute__((always_inline)) {
+    if (k_copy && v_copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave + WT::kVLoadsPerWave));
+    else if (k_copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave));
+    else if (v_copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kVLoadsPerWave));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+  };
+  // a step with a piece missing (the first and last ones of an item): the
+  // pieces one after another, with the MFMA wait states made explicit
+  auto step_general = [&](int u, auto par_tag, const char* ks, const char* vs)
+                          __attribute__((always_inline)) {
+    constexpr int par = decltype(par_tag)::value;
+    constexpr int h = par ^ 1;
+    wide_settle_o(ta, tb);
+    if (u >= 1 && u - 1 < n_half) {
+      asm volatile(FMHA_MFMA_SETTLE : "+v"(ta.hp[h][0]), "+v"(ta.hp[h][1]), "+v"(tb.hp[h][0]),
+                   "+v"(tb.hp[h][1]));
+      wide_pv<h>(ta, tb, vs);
+    }
+    if (u + 1 < n_half) wide_qk<h>(ta, tb, ks);
+    if (u >= 0 && u < n_half) {
+      mfma_settle_s(ta, tb, par);
+      ta.mask_half(ta.hs[par], u, w.sk, causal_off);
+      tb.mask_half(tb.hs[par], u, w.sk, causal_off);
+      const float la = ta.exp_half(ta.hs[par], ta.hp[par]);
+      const float lb = tb.exp_half(tb.hs[par], tb.hp[par]);
+      ta.settle_half(ta.hs[par], ta.hp[par], la);
+      tb.settle_half(tb.hs[par], tb.hp[par], lb);
+    }
+  };
+  // iteration i reads K tile i (stage i % 3) and V tile i-1 (stage (i+2) % 3)
+  auto iteration_general = [&](int i) __attribute__((always_inline)) {
+    const bool k_copy = i + 2 < n_tiles, v_copy = i + 1 < n_tiles;
+    copies_rt(i);
+    const char* ks = smem_k[i % kStagesWide];
+    const char* vs = smem_v[(i + 2) % kStagesWide];
+    step_general(2 * i - 1, std::integral_constant<int, 1>(), ks, vs);
+    step_general(2 * i, std::integral_constant<int, 0>(), ks, vs);
+    finish_iteration(k_copy, v_copy);
+  };
+  // steady state: both steps have all three pieces; kSt = i % 3
+  auto iteration_steady = [&](int i, auto st_tag) __attribute__((always_inline)) {
+    constexpr int kSt = decltype(st_tag)::value;
+    const bool k_copy = i + 2 < n_tiles, v_copy = i + 1 < n_tiles;
+    if (k_copy) ta.template copy_k<(kSt + 2) % kStagesWide>(i + 2, k_lds0);
+    if (v_copy) ta.template copy_v<(kSt + 1) % kStagesWide>(i + 1, v_lds0);
+    const char* ks = smem_k[kSt];
+    const char* vs = smem_v[(kSt + 2) % kStagesWide];
+    wide_settle_o(ta, tb);
+    ta.mask_half(ta.hs[1], 2 * i - 1, w.sk, causal_off);
+    tb.mask_half(tb.hs[1], 2 * i - 1, w.sk, causal_off);
+    float2 ls = wide_step<1>(ta, tb, ks, vs);
+    ta.settle_half(ta.hs[1], ta.hp[1], ls.x);
+    tb.settle_half(tb.hs[1], tb.hp[1], ls.y);
+    wide_settle_o(ta, tb);
+    ta.mask_half(ta.hs[0], 2 * i, w.sk, causal_off);
+    tb.mask_half(tb.hs[0], 2 * i, w.sk, causal_off);
+    ls = wide_step<0>(ta, tb, ks, vs);
+    ta.settle_half(ta.hs[0], ta.hp[0], ls.x);
+    tb.settle_half(tb.hs[0], tb.hp[0], ls.y);
+    finish_iteration(k_copy, v_copy);
+  };
+
+  if (n_tiles > 0) {
+    // prologue: K tiles 0 and 1, V tile 0; Q and K tile 0 land first
+    ta.template copy_k<0>(0, k_lds0);
+    if (n_tiles > 1) ta.template copy_k<1>(1, k_lds0);
+    ta.template copy_v<0>(0, v_lds0);
+    if (n_tiles > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kLoadsPerWave + WT::kVLoadsPerWave));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT::kVLoadsPerWave));
+    mfma_settle_q(ta, tb);
+    lds_barrier();
+    // iterations 0 .. ceil(n_half / 2); the last one holds the final P.V.
+    // Iterations 1 .. last_steady have every piece of both steps.
+    const int n_iter = (n_half + 1) / 2 + 1;
+    const int last_steady = (n_half - 2) / 2;
+    iteration_general(0);
+    int i = 1;
+    for (; i + 2 <= last_steady; i += 3) {
+      iteration_steady(i, std::integral_constant<int, 1>());
+      iteration_steady(i + 1, std::integral_constant<int, 2>());
+      iteration_steady(i + 2, std::integral_constant<int, 0>());
+    }
+    if (i <= last_steady) {
+      iteration_steady(i, std::integral_constant<int, 1>());
+      ++i;
+    }
+    if (i <= last_steady) {
+      iteration_steady(i, std::integral_constant<int, 2>());
+      ++i;
+    }
+    for (; i < n_iter; ++i) iteration_general(i);
+  }
+
+  mfma_settle_o(ta, tb);
+  if constexpr (kStageO) {
+    ta.template epilogue_lds<1024>(p, w, lds_address(&smem_o[4096 * wave]));
+    tb.template epilogue_lds<1024>(p, w, lds_address(&smem_o[4096 * wave]));
+  } else {
+    ta.epilogue(p, w);
+    tb.epilogue(p, w);
+  }
+  };
+  for_each_item<kCausal, false>(params, run_item);
+}
+
 // ---------------------------------------------------------------- launchers
 
 // Compute units of the current device (cached per device; the attribute query
@@ -581,7 +997,8 @@ static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   if (!kSplit) q.num_splits = 1;
   const int variant_run = resolve_variant(variant, p.batch, p.max_seqlen_q, p.heads, q.num_splits);
   const bool use8 = variant_run == kVariantPingPong;
-  const int bm = use8 ? kBM8 : kBM4;
+  const bool one_per_cu = use8 || variant_run == kVariantWide;
+  const int bm = use8 ? kBM8 : variant_run == kVariantWide ? kBMWide : kBM4;
   q.n_mblocks = (p.max_seqlen_q + bm - 1) / bm;
   const long long n_items = (long long)q.n_mblocks * p.heads * p.batch * q.num_splits;
   if (n_items == 0) return hipSuccess;
@@ -589,13 +1006,19 @@ static hipError_t launch(const FwdParams& p, int variant, hipStream_t stream) {
   // causal kernels are persistent: as many workgroups as the chip holds at once
   // (one per CU for the 8-wave kernel, two for the 4-wave ones), a multiple of
   // the XCD count; the others take one item per workgroup
-  const long long resident = (long long)device_cus() * (use8 ? 1 : 2);
+  const long long resident = (long long)device_cus() * (one_per_cu ? 1 : 2);
   const long long grid =
       kCausal ? (std::min(n_items, resident) + kXcds - 1) / kXcds * kXcds : n_items;
   if (variant_run == kVariantPipelined) {
     if constexpr (kPv == kPvBf16 && !kSplit)
       hipLaunchKernelGGL((fmha_fwd_pipe_kernel<kD, kCausal>), dim3((unsigned)grid),
                          dim3(kWavesPipe * 64), 0, stream, q);
+    else
+      return hipErrorInvalidValue;
+  } else if (variant_run == kVariantWide) {
+    if constexpr (kPv == kPvBf16 && !kSplit)
+      hipLaunchKernelGGL((fmha_fwd_wide_kernel<kD, kCausal>), dim3((unsigned)grid),
+                         dim3(kWavesWide * 64), 0, stream, q);
     else
       return hipErrorInvalidValue;
   } else if (use8)

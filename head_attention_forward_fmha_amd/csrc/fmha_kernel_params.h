@@ -63,11 +63,13 @@ constexpr int kVariantAuto = 0;      // pick by problem size
 constexpr int kVariantFourWave = 1;  // 4 waves, 128 query rows per workgroup
 constexpr int kVariantPingPong = 2;  // 8 waves in two phase-shifted groups, 256 rows
 constexpr int kVariantPipelined = 3; // 4 waves, each software-pipelined (bf16 only)
+constexpr int kVariantWide = 4;      // 4 waves of 64 rows, one per SIMD (bf16 only)
 
 // Query rows per workgroup of each kernel.
 constexpr int kRowsFourWave = 128;
 constexpr int kRowsPingPong = 256;
 constexpr int kRowsPipelined = 128;
+constexpr int kRowsWide = 256;
 
 // The kernel a launch runs. Automatic selection takes the 8-wave kernel once the
 // problem has at least 128 work items of 256 query rows (half the CUs of an

@@ -149,15 +149,21 @@ fmha_status_t fmha_fwd_fp4pv(const void* q, const void* k, const uint8_t* v_e2m1
  * fmha_fwd, fmha_fwd_fp8pv and fmha_fwd_fp4pv use) takes the 8-wave ping-pong kernel when the
  * problem has at least 128 blocks of 256 query rows, else the 4-wave kernel;
  * fmha_fwd_splitkv counts each block num_splits times.
- * All variants compute the same function. They currently run the same per-row
- * arithmetic in the same key-tile order and give bit-identical results; the ABI
- * promises only agreement within rounding.
+ * All variants compute the same function. The 4-wave and ping-pong kernels run
+ * the same per-row arithmetic in the same key-tile order and give bit-identical
+ * results; the pipelined and 64-row-wave kernels take the lazy row-maximum
+ * decision per 32 keys and agree with them within rounding, which is all the
+ * ABI promises.
  */
 #define FMHA_VARIANT_AUTO 0
 #define FMHA_VARIANT_FOUR_WAVE 1   /* 4 waves, 128 query rows per workgroup   */
 #define FMHA_VARIANT_PINGPONG 2    /* 8 waves in two phase-shifted groups     */
 #define FMHA_VARIANT_PIPELINED 3   /* 4 waves, each software-pipelined; bf16
                                       only (fp8/fp4 P.V: FMHA_ERR_UNSUPPORTED) */
+#define FMHA_VARIANT_WIDE 4        /* 4 waves of 64 query rows, one per SIMD,
+                                      each K/V operand read feeding two MFMAs;
+                                      bf16 only (fp8/fp4 P.V, split-KV:
+                                      FMHA_ERR_UNSUPPORTED) */
 
 /* fmha_fwd with an explicit kernel variant (any other value: INVALID_ARG). */
 fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,
@@ -168,7 +174,8 @@ fmha_status_t fmha_fwd_variant(const void* q, const void* k, const void* v,
                                int32_t causal, float softmax_scale,
                                void* out, float* lse, int32_t variant, void* stream);
 
-/* fmha_fwd_fp8pv with an explicit kernel variant (any other value: INVALID_ARG). */
+/* fmha_fwd_fp8pv with an explicit kernel variant (any other value: INVALID_ARG;
+ * FMHA_VARIANT_PIPELINED, FMHA_VARIANT_WIDE: FMHA_ERR_UNSUPPORTED). */
 fmha_status_t fmha_fwd_fp8pv_variant(const void* q, const void* k, const uint8_t* v_e4m3,
                                      const float* v_scale,
                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -179,7 +186,7 @@ fmha_status_t fmha_fwd_fp8pv_variant(const void* q, const void* k, const uint8_t
                                      void* out, float* lse, int32_t variant, void* stream);
 
 /* fmha_fwd_fp4pv with an explicit kernel variant (any other value: INVALID_ARG;
- * FMHA_VARIANT_PIPELINED: FMHA_ERR_UNSUPPORTED). */
+ * FMHA_VARIANT_PIPELINED, FMHA_VARIANT_WIDE: FMHA_ERR_UNSUPPORTED). */
 fmha_status_t fmha_fwd_fp4pv_variant(const void* q, const void* k, const uint8_t* v_e2m1,
                                      const uint8_t* v_mx_scale,
                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -206,8 +213,8 @@ fmha_status_t fmha_fwd_fp4pv_variant(const void* q, const void* k, const uint8_t
  *                    [num_splits, total_q, num_heads, head_dim], then LSE parts
  *                    fp32 [num_splits, num_heads, total_q]. Calls that share a
  *                    workspace must not overlap.
- *   variant          FMHA_VARIANT_AUTO, _FOUR_WAVE or _PINGPONG (_PIPELINED:
- *                    FMHA_ERR_UNSUPPORTED)
+ *   variant          FMHA_VARIANT_AUTO, _FOUR_WAVE or _PINGPONG (_PIPELINED,
+ *                    _WIDE: FMHA_ERR_UNSUPPORTED)
  * Every other argument as for fmha_fwd.
  */
 fmha_status_t fmha_fwd_splitkv(const void* q, const void* k, const void* v,

@@ -94,13 +94,14 @@ def test_variant_must_be_known():
     lib = fm.load_library()
     args = [0x10000, 0x20000, 0x30000, None, None, 1, 128, 128, 128, 128, 2, 64, 0,
             ctypes.c_float(0.125), 0x40000, 0x50000]
-    assert lib.fmha_fwd_variant(*args, 4, None) == 1
+    assert lib.fmha_fwd_variant(*args, 5, None) == 1
     assert lib.fmha_fwd_variant(*args, -1, None) == 1
     fargs = [0x10000, 0x20000, 0x30000, 0x70000, None, None, 1, 128, 128, 128, 128, 2, 128, 0,
              ctypes.c_float(0.125), 0x40000, 0x50000]
     assert lib.fmha_fwd_fp8pv_variant(*fargs, 7, None) == 1
-    # the pipelined kernel has no fp8 P.V form
+    # the pipelined and 64-row-wave kernels have no fp8 P.V form
     assert lib.fmha_fwd_fp8pv_variant(*fargs, 3, None) == 2
+    assert lib.fmha_fwd_fp8pv_variant(*fargs, 4, None) == 2
 
 
 @pytest.mark.parametrize("batch,max_q,heads,want", [
@@ -159,6 +160,7 @@ def test_fp4_argument_checks():
     args[2] = 0x30000
     vargs = args[:-1]
     assert lib.fmha_fwd_fp4pv_variant(*vargs, 3, None) == 2   # no pipelined fp4 kernel
+    assert lib.fmha_fwd_fp4pv_variant(*vargs, 4, None) == 2   # nor a 64-row-wave one
     assert lib.fmha_fwd_fp4pv_variant(*vargs, 5, None) == 1
     # nothing to compute: no launch, no GPU needed
     empty = [None, None, None, None, None, None, 0, 0, 0, 0, 0, 2, 128, 1,
@@ -178,7 +180,7 @@ def test_splitkv_argument_checks():
     need = fm.splitkv_workspace_size(128, 2, 64, 2)
     ok_tail = [2, 0x80000, need, 0, None]
     for i, bad, status in ((0, 0, 1), (0, 65, 1), (1, None, 1), (1, 0x80008, 1),
-                           (2, need - 1, 1), (3, 3, 2), (3, 9, 1)):
+                           (2, need - 1, 1), (3, 3, 2), (3, 4, 2), (3, 9, 1)):
         tail = list(ok_tail)
         tail[i] = bad
         assert lib.fmha_fwd_splitkv(*base, *tail) == status, (i, bad)

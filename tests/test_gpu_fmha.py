@@ -33,8 +33,8 @@ from tests.parity import NORMALISED_BAR, error_summary, fp8_emulation_check
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["four_wave", "pingpong", "pipelined"]
-VARIANTS_FP8 = ["four_wave", "pingpong"]   # the pipelined kernel is bf16 only
+VARIANTS = ["four_wave", "pingpong", "pipelined", "wide"]
+VARIANTS_FP8 = ["four_wave", "pingpong"]   # the pipelined and 64-row-wave kernels are bf16 only
 
 O_ATOL = O_RTOL = 1e-2
 O_ATOL_FP8 = O_RTOL_FP8 = 5e-2
@@ -209,7 +209,7 @@ def test_c2_dense_layout_matches_packed():
     assert torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("variant", ["auto", "pipelined"])
+@pytest.mark.parametrize("variant", ["auto", "pipelined", "wide"])
 def test_c3_varlen_causal_8k_full(variant):
     """c3 at full size, every (token, head, d) output against the full oracle."""
     w = WORKLOADS["c3_varlen_causal_8k"]
@@ -246,13 +246,15 @@ def test_c4_varlen_causal_32k_full():
     _check(o, lse, o_ref, lse_ref, what=w.name)
 
 
-def test_c4_varlen_causal_32k_sampled_pipelined():
-    _sampled_parity(WORKLOADS["c4_varlen_causal_32k"], n_random=1000, variant="pipelined")
+@pytest.mark.parametrize("variant", ["pipelined", "wide"])
+def test_c4_varlen_causal_32k_sampled_variant(variant):
+    _sampled_parity(WORKLOADS["c4_varlen_causal_32k"], n_random=1000, variant=variant)
 
 
-def test_c2_dense_2225_pipelined():
+@pytest.mark.parametrize("variant", ["pipelined", "wide"])
+def test_c2_dense_2225_variant(variant):
     w = WORKLOADS["c2_dense_2225"]
-    _full_parity(w.doc_lens, w.heads, w.head_dim, w.causal, variant="pipelined")
+    _full_parity(w.doc_lens, w.heads, w.head_dim, w.causal, variant=variant)
 
 
 def test_c5_causal_fp8pv_32k_sampled():
@@ -308,7 +310,7 @@ def _edge_mix(n_random, max_len, seed):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("variant", ["four_wave", "pingpong"])
+@pytest.mark.parametrize("variant", ["four_wave", "pingpong", "wide"])
 def test_persistent_items_with_edge_documents(d, variant):
     # 40 documents x 16 heads x 3 blocks of 256 rows: far more items than the
     # 256 workgroups of the persistent grid, empty ones included
@@ -421,13 +423,14 @@ def test_causal_row0_is_v0_exactly(variant):
         assert torch.allclose(l[:, a].double().cpu(), ref, atol=1e-4, rtol=0)
 
 
-def test_pipelined_rejects_fp8():
+@pytest.mark.parametrize("variant", ["pipelined", "wide"])
+def test_bf16_only_variants_reject_fp8(variant):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     inp = make_inputs(((128, 128),), 2, 128, seed=31, fp8_pv=True)
     with pytest.raises(fm.FmhaError):
         fm.fwd_fp8pv(inp.q.to(dev), inp.k.to(dev), inp.v_e4m3.to(dev), inp.v_scale.to(dev),
-                     variant="pipelined")
+                     variant=variant)
 
 
 # ---------------------------------------------------------------- stale LDS

@@ -185,13 +185,14 @@ def test_fp4_deterministic_repeats(variant):
         assert np.array_equal(o, o0) and np.array_equal(l, l0)
 
 
-def test_fp4_pipelined_is_rejected():
+@pytest.mark.parametrize("variant", ["pipelined", "wide"])
+def test_fp4_bf16_only_variants_are_rejected(variant):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     inp = make_inputs(((128, 128),), 2, 128, seed=31, fp4_pv=True)
     with pytest.raises(fm.FmhaError):
         fm.fwd_fp4pv(inp.q.to(dev), inp.k.to(dev), inp.v_e2m1.to(dev), inp.v_mx_scale.to(dev),
-                     variant="pipelined")
+                     variant=variant)
 
 
 @pytest.mark.parametrize("variant", VARIANTS_FP4)

@@ -185,13 +185,14 @@ def test_splitkv_deterministic_repeats():
         assert np.array_equal(o, o0) and np.array_equal(l, l0)
 
 
-def test_splitkv_pipelined_is_rejected():
+@pytest.mark.parametrize("variant", ["pipelined", "wide"])
+def test_splitkv_unsplit_only_variants_are_rejected(variant):
     import head_attention_forward_fmha_amd as fm
     dev = _dev()
     inp = make_inputs(((128, 128),), 2, 128, seed=31)
     with pytest.raises(fm.FmhaError):
         fm.fwd_splitkv(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), num_splits=2,
-                       variant="pipelined")
+                       variant=variant)
 
 
 @pytest.mark.parametrize("causal", [False, True])
