@@ -60,7 +60,7 @@ CSRC = os.path.join(ROOT, "head_attention_forward_fmha_amd", "csrc")
 KERNEL_SOURCES = ("fmha_fwd_kernel.hip", "fmha_device.h", "fmha_kernel_params.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fmha_fwd_traffic.json")
 KERNEL_NAMES = {"four_wave": "fmha::fmha_fwd_kernel", "pingpong": "fmha::fmha_fwd_pingpong_kernel",
-                "pipelined": "fmha::fmha_fwd_pipe_kernel"}
+                "pipelined": "fmha::fmha_fwd_pipe_kernel", "wide": "fmha::fmha_fwd_wide_kernel"}
 # counted FLOP of the oracle sample: about 10-30 s of fp64 numpy on a 16-core host
 CPU_SAMPLE_FLOP = 4e11
 
@@ -83,7 +83,7 @@ def pv_format(w) -> int:
 
 
 def kernel_template_name(w, variant, split=False):
-    if variant == "pipelined":
+    if variant in ("pipelined", "wide"):
         return f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}>"
     return (f"{KERNEL_NAMES[variant]}<{w.head_dim}, {str(w.causal).lower()}, {pv_format(w)}, "
             f"{str(split).lower()}>")
@@ -118,7 +118,7 @@ def parse_args():
                     choices=sorted(SHORT) + sorted(SHORT.values()) +
                     ["x_varlen_noncausal_32k", "x_short_q_long_k", "x_causal_fp4pv_32k",
                      "x_causal_bf16_32k"])
-    ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong", "pipelined"],
+    ap.add_argument("--variant", default="auto", choices=["auto", "four_wave", "pingpong", "pipelined", "wide"],
                     help="kernel variant (auto picks by problem size)")
     ap.add_argument("--splits", default=None,
                     help="run the split-KV pass (bf16) with this many key splits, or 'auto'; "
@@ -576,7 +576,8 @@ def main():
         c = summarize_counters(*args.summarize_counters)
         kernel = c["FETCH_SIZE"]["kernel"]
         variant = ("pingpong" if "pingpong" in kernel else
-                   "pipelined" if "pipe_kernel" in kernel else "four_wave")
+                   "pipelined" if "pipe_kernel" in kernel else
+                   "wide" if "wide_kernel" in kernel else "four_wave")
         table = {}
         if os.path.exists(TRAFFIC_FILE):
             with open(TRAFFIC_FILE) as f:

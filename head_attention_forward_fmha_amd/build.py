@@ -95,6 +95,7 @@ _MANGLED_PREFIX = {
     "pingpong": "_ZN4fmha24fmha_fwd_pingpong_kernel",
     "four_wave": "_ZN4fmha15fmha_fwd_kernel",
     "pipelined": "_ZN4fmha20fmha_fwd_pipe_kernel",
+    "wide": "_ZN4fmha20fmha_fwd_wide_kernel",
     "bwd_dkdv": "_ZN4fmha12_GLOBAL__N_120fmha_bwd_dkdv_kernel",
     "bwd_dq": "_ZN4fmha12_GLOBAL__N_118fmha_bwd_dq_kernel",
 }
@@ -112,7 +113,7 @@ def mangled_kernel_name(family: str, head_dim: int, causal: bool = False, pv: in
         return (f"{pre}ILi{head_dim}{b(causal)}ELi{pv}{b(split)}ENS_12NoPhaseTraceEEEvNS_9FwdParamsE")
     if family == "four_wave":
         return f"{pre}ILi{head_dim}{b(causal)}ELi{pv}{b(split)}EEEvNS_9FwdParamsE"
-    if family == "pipelined":
+    if family in ("pipelined", "wide"):
         return f"{pre}ILi{head_dim}{b(causal)}EEEvNS_9FwdParamsE"
     return f"{pre}ILi{head_dim}{b(causal)}EEEvNS_9BwdParamsE"
 
