@@ -15,9 +15,9 @@ Every check also reports the error normalised by the row RMS of O_ref and
 holds it to a derived bar (tests/parity.py), which stays sharp on long rows.
 
 The five workloads are checked at their full sizes in the launch configuration
-the benchmark times: c1, c2, c3 and c4 on every output, c5 on sampled
-(token, head) rows the oracle computes one by one (each from its complete score
-row). Edge cases cover ragged tails, empty documents, sq != sk with causal
+the benchmark times: c1, c2, c3 and c4 on every output, c5 on every row of one
+head and on sampled (token, head) rows of all heads, which the oracle computes
+one by one (each from its complete score row). Edge cases cover ragged tails, empty documents, sq != sk with causal
 bottom-right alignment, d = 64, and tiny documents.
 """
 
@@ -261,6 +261,34 @@ def test_c5_causal_fp8pv_32k_sampled():
     """c5 at full size on sampled rows: the stated fp8 bar against the exact
     attention of the dequantised V, and the emulated method at the bf16 bar."""
     _sampled_parity(WORKLOADS["c5_causal_fp8pv_32k"], n_random=600)
+
+
+@pytest.mark.timeout(600)
+def test_c5_causal_fp8pv_32k_one_head_every_row():
+    """c5 at full size: every row of one head (all 32768, so every position of
+    the long persistent items) at the stated fp8 bar against the exact
+    attention of the dequantised V, and every other row of that head against
+    the emulated method at the bf16 bar."""
+    w = WORKLOADS["c5_causal_fp8pv_32k"]
+    inp = workload_inputs(w)
+    o, lse = _run(inp, w.causal, w.softmax_scale, w.heads, w.head_dim, fp8=True)
+    head = 5
+    rows = np.arange(int(inp.cu_q[-1]))
+    print("c5: exact oracle on every row of one head", flush=True)
+    o_ref, l_ref = oracle.attention_fp8pv_sampled(inp.q, inp.k, inp.v_e4m3, inp.v_scale,
+                                                  inp.cu_q, inp.cu_k, w.causal, w.softmax_scale,
+                                                  [(int(t), head) for t in rows])
+    err = np.abs(o[rows, head] - o_ref)
+    tol = O_ATOL_FP8 + O_RTOL_FP8 * np.abs(o_ref)
+    assert (err <= tol).all(), f"{int((err > tol).sum())} O elements of head {head} off the bar"
+    assert np.abs(lse[head, rows] - l_ref).max() <= LSE_ATOL
+    sub = rows[::2]
+    print("c5: emulated method on every other row of that head", flush=True)
+    emu = oracle.attention_fp8pv_emulated(inp.q, inp.k, inp.v_e4m3, inp.v_scale, inp.cu_q,
+                                          inp.cu_k, w.causal, w.softmax_scale,
+                                          samples=[(int(t), head) for t in sub])
+    _check(o[sub, head], lse[head, sub], o_ref[::2], l_ref[::2], fp8=True, emu=emu,
+           what=f"{w.name} head {head}")
 
 
 # ---------------------------------------------------------------- edge cases
