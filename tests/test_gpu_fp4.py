@@ -165,6 +165,25 @@ def test_fp4_x_causal_32k_sampled():
     _check(o[t, hh], lse[hh, t], emu, o_x, l_x, what=w.name)
 
 
+@pytest.mark.timeout(600)
+def test_fp4_x_causal_32k_one_head_every_8th_row():
+    """The 32768-token single-document causal fp4 workload at full size: every
+    8th row of one head, so positions across the whole length of the long
+    persistent items, against the emulated method and the exact bound."""
+    w = EXTRA_WORKLOADS["x_causal_fp4pv_32k"]
+    inp = workload_inputs(w)
+    o, lse = _run(inp, w.causal, w.softmax_scale, w.heads)
+    head = 11
+    samples = [(int(t), head) for t in range(0, w.total_q, 8)]
+    print("fp4 32k: emulated method on every 8th row of one head", flush=True)
+    emu = oracle.attention_fp4pv_emulated(inp.q, inp.k, inp.v_e2m1, inp.v_mx_scale, inp.cu_q,
+                                          inp.cu_k, True, w.softmax_scale, samples=samples)
+    o_x, l_x = oracle.attention_fp4pv_sampled(inp.q, inp.k, inp.v_e2m1, inp.v_mx_scale, inp.cu_q,
+                                              inp.cu_k, True, w.softmax_scale, samples)
+    t = np.array([a for a, _ in samples])
+    _check(o[t, head], lse[head, t], emu, o_x, l_x, what=f"{w.name} head {head}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp4_kernel_variants_agree_bitwise(causal):
     lens = ((1000, 1000), (333, 333), (1, 1), (700, 701))
