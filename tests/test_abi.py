@@ -345,3 +345,12 @@ def test_built_kernels_have_no_scratch_or_spills():
     kernels = parse_resource_report(open(RESOURCE_REPORT).read())
     assert sum("fmha_fwd" in k for k in kernels) >= 16
     assert check_resources(kernels) == []
+
+
+def test_binding_variant_names_match_the_header():
+    """The binding's variant names map to the values include/fmha.h defines."""
+    from head_attention_forward_fmha_amd import _lib
+    header = open(os.path.join(ROOT, "include", "fmha.h")).read()
+    defined = {m.group(1).lower(): int(m.group(2))
+               for m in re.finditer(r"#define FMHA_VARIANT_(\w+) (\d+)", header)}
+    assert defined == _lib.VARIANTS
