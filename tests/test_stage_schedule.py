@@ -1,4 +1,5 @@
-"""The LDS stage schedule of the 64-row-wave forward kernel, checked on the CPU.
+"""The LDS stage schedules of the forward kernels, checked on the CPU: the
+64-row-wave kernel's iterations and the ping-pong kernel's slots (below).
 
 The kernel walks a work item's keys in half-tiles of 32 through iterations of
 two steps: step u runs the softmax of half-tile u, Q.K^T of half-tile u+1 and
@@ -95,3 +96,87 @@ def test_the_model_reports_a_copy_one_tile_too_early():
            for r, cp in iters]
     with pytest.raises(AssertionError):
         check_schedule(12, [(k, t, t % 2) for k, t, _ in prologue], two)
+
+
+# ---------------------------------------------------------------- the ping-pong kernel
+#
+# Two groups of waves, half a tile apart. Tile j lives in stage j % 3. Slot 2j:
+# group A runs Q.K^T of tile j and P.V of tile j-1 (MFMA phase) while group B
+# runs the softmax of tile j-1 and first copies K tile j+2; slot 2j+1: group B
+# runs Q.K^T of tile j and P.V of tile j-1 while group A runs the softmax of
+# tile j and first copies V tile j+1. A group waits for its own earlier copies
+# at the end of its softmax slot (all but the ones it issued in that slot), and
+# every slot ends with a workgroup barrier. The prologue copies K tiles 0 and 1
+# and V tile 0 and waits for all of them; a last slot pair j = n runs the P.V
+# of tile n-1.
+
+def pingpong_schedule(n):
+    """Slots of an item with n key tiles: (reads, copies, landed) per slot, where
+    landed lists the copies whose wait ends this slot (visible from the next)."""
+    slots = []
+    pending = {"A": [], "B": []}
+    for j in range(n + 1):
+        for half in (0, 1):
+            mfma, valu = ("A", "B") if half == 0 else ("B", "A")
+            reads, copies = [], []
+            if j < n:
+                reads.append((mfma, "K", j, j % STAGES))
+            if 1 <= j:
+                reads.append((mfma, "V", j - 1, (j - 1) % STAGES))
+            if half == 0 and j + 2 < n:
+                copies.append((valu, "K", j + 2, (j + 2) % STAGES))
+            if half == 1 and j + 1 < n:
+                copies.append((valu, "V", j + 1, (j + 1) % STAGES))
+            # the softmax group's wait: every copy it issued before this slot
+            landed = pending[valu]
+            pending[valu] = [c for c in copies if c[0] == valu]
+            slots.append((reads, copies, landed))
+    return slots
+
+
+def check_pingpong(n, slots):
+    prologue = ([("K", 0, 0), ("V", 0, 0)] if n >= 1 else []) + ([("K", 1, 1)] if n >= 2 else [])
+    holder = {(k, st): t for k, t, st in prologue}
+    visible = {(k, t) for k, t, _ in prologue}
+    last_read = {}
+    for s, (reads, _, _) in enumerate(slots):
+        for _g, k, t, _st in reads:
+            last_read[(k, t)] = s
+    for s, (reads, copies, landed) in enumerate(slots):
+        for _g, k, t, st in copies:
+            old = holder.get((k, st))
+            assert old is None or last_read.get((k, old), -1) < s, (n, s, k, t, old)
+            holder[(k, st)] = t
+        for _g, k, t, st in reads:
+            assert holder.get((k, st)) == t and (k, t) in visible, (n, s, k, t)
+        for _g, k, t, _st in landed:
+            visible.add((k, t))
+
+
+@pytest.mark.parametrize("n", range(0, 24))
+def test_pingpong_stage_ring_is_race_free(n):
+    check_pingpong(n, pingpong_schedule(n))
+
+
+def test_pingpong_model_reports_a_late_wait():
+    """Planted mistake: a group that waits for its copies one softmax slot later
+    than the kernel does reads a K tile that has not landed."""
+    slots = pingpong_schedule(9)
+    late = [(r, c, []) for r, c, _ in slots]
+    for s in range(len(slots) - 2):
+        late[s + 2] = (late[s + 2][0], late[s + 2][1], late[s + 2][2] + slots[s][2])
+    with pytest.raises(AssertionError):
+        check_pingpong(9, late)
+
+
+def test_pingpong_model_reports_a_copy_one_tile_too_early():
+    """Planted mistake: K tile j+3 copied in slot 2j lands in the stage that K
+    tile j is read from in that slot."""
+    slots = pingpong_schedule(9)
+    early = []
+    for reads, copies, landed in slots:
+        copies = [(g, k, t + 1, (t + 1) % STAGES) if k == "K" else (g, k, t, st)
+                  for g, k, t, st in copies]
+        early.append((reads, copies, landed))
+    with pytest.raises(AssertionError):
+        check_pingpong(9, early)
