@@ -572,8 +572,8 @@ void fmha_fwd_pipe_kernel(FwdParams params) {
 // same work), and gives every K and V operand it reads from LDS to two MFMAs,
 // one per block: half the LDS bytes per MFMA of the 32-row kernels. The wave
 // software-pipelines its work over half-tiles of 32 keys as the pipelined
-// kernel does: step u runs the softmax of half-tile u (vector ALU), S of
-// half-tile u+1 (Q.K^T MFMAs, then) and O += P V of half-tile u-1 (P.V MFMAs).
+// kernel does: step u runs the softmax of half-tile u (vector ALU) beside the
+// Q.K^T MFMAs of half-tile u+1 and then the P.V MFMAs of half-tile u-1.
 //
 // Register files. Q (the B operand of S^T = K Q^T) and O^T (the accumulator
 // of O^T += V^T P^T) live in the accumulation registers (AGPRs), S^T and P in
@@ -581,11 +581,12 @@ void fmha_fwd_pipe_kernel(FwdParams params) {
 // is read from and written to the file it lives in, without copies between
 // the files. The compiler therefore does not see them: the wait states the
 // ISA requires between an MFMA and a later instruction that reads or
-// overwrites its result (at most 19 for these 8-pass MFMAs), or between a
-// vector write of an operand and the MFMA that reads it, come from the
-// schedule (in a steady step, the 16 P.V MFMAs issued after the last Q.K^T
-// MFMA of a half-tile keep its S from being read before the next step) or
-// from mfma_settle where the schedule does not provide them.
+// overwrites its result, or between a vector write of an operand and the MFMA
+// that reads it, come from the schedule (in a steady step, the 16 P.V MFMAs
+// issued after the last Q.K^T MFMA of a half-tile keep its S from being read
+// before the next step) or from mfma_settle (24 wait states, more than the
+// ISA's hazard tables ask for after these MFMAs) where the schedule does not
+// provide them.
 constexpr int kWavesWide = 4;
 constexpr int kBMWide = kWavesWide * 64;  // query rows per workgroup
 static_assert(kBMWide == kRowsWide, "64-row-wave block height");
